@@ -1,0 +1,142 @@
+"""Oracle for the fused attention forward: plain fp64 CPU evaluation.
+
+TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
+this package.  It shares no code with the HIP library and never imports it.
+
+The arithmetic lives in ``attn_oracle.c`` (single-threaded C, libm exp/log,
+fp64).  This module only compiles that file with gcc, loads it with ctypes and
+hands it buffers.  ``threads > 1`` splits the list of query rows between host
+threads, each running the same single-threaded C routine on its own rows (the
+rows are independent, so the result does not depend on the split).
+
+What is computed, per head (b, h) and query row i (ThunderKittens write-up,
+88811315.cn, "RTX 4090 flash-attention example" / "H100 FlashAttention-2
+forward example": the fixed point of the running-max recurrence):
+
+    s_j = scale * q_i . k_j   for visible j  (all j, or j <= i when causal)
+    o_i = sum_j softmax(s)_j v_j,   lse_i = ln sum_j exp(s_j)
+
+Inputs are bf16 bit patterns in numpy ``uint16`` arrays of shape [B, H, N, d].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import tempfile
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "attn_oracle.c")
+LIBRARY = os.path.join(_HERE, "libattn_oracle.so")
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile the oracle with gcc -O2 (no fast-math) into a shared library."""
+    out_dir = os.path.dirname(os.path.abspath(output))
+    fd, tmp = tempfile.mkstemp(suffix=".so.tmp", dir=out_dir)
+    os.close(fd)
+    try:
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c99", "-fno-fast-math", "-fPIC", "-shared",
+             "-o", tmp, source, "-lm"])
+        os.replace(tmp, output)
+    finally:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+    return output
+
+
+def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    i64, u16p, f64p = ctypes.c_int64, ctypes.POINTER(ctypes.c_uint16), ctypes.POINTER(ctypes.c_double)
+    lib.attn_oracle_rows.argtypes = [
+        u16p, u16p, u16p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double,
+        ctypes.POINTER(ctypes.c_int64), i64, f64p, f64p]
+    lib.attn_oracle_rows.restype = ctypes.c_int
+    return lib
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load a compiled oracle.  With no path: the in-tree library, built here
+    first if it is missing or older than its source."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            stale = (not os.path.exists(LIBRARY)
+                     or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE))
+            if stale:
+                build()
+            _lib = _declare(ctypes.CDLL(LIBRARY))
+    return _lib
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _check_inputs(q, k, v):
+    for name, a in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(a, np.ndarray) or a.dtype != np.uint16 or a.ndim != 4:
+            raise TypeError(f"{name} must be a 4-D numpy uint16 array of bf16 bits")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k and v must have the same shape [B, H, N, d]")
+    return (np.ascontiguousarray(q), np.ascontiguousarray(k), np.ascontiguousarray(v))
+
+
+def attention_rows(q, k, v, causal: bool, scale: float, rows, threads: int = 1,
+                   lib: ctypes.CDLL | None = None):
+    """Oracle output for the listed query rows.
+
+    ``rows`` holds flat row indices r = (b*H + h)*N + i.  Returns
+    ``(o, lse)`` with ``o`` float64 [len(rows), d] and ``lse`` float64 [len(rows)].
+    """
+    q, k, v = _check_inputs(q, k, v)
+    B, H, N, d = q.shape
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+    if rows.size and (rows.min() < 0 or rows.max() >= B * H * N):
+        raise ValueError("row index out of range")
+    lib = lib or load()
+    o = np.zeros((rows.size, d), dtype=np.float64)
+    lse = np.zeros(rows.size, dtype=np.float64)
+    threads = max(1, min(int(threads), rows.size or 1))
+    bounds = np.linspace(0, rows.size, threads + 1).astype(np.int64)
+
+    def run(part):
+        lo, hi = int(bounds[part]), int(bounds[part + 1])
+        if hi <= lo:
+            return 0
+        sub_rows = rows[lo:hi]
+        sub_o = o[lo:hi]
+        sub_lse = lse[lo:hi]
+        return lib.attn_oracle_rows(
+            _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
+            B, H, N, d, int(bool(causal)), float(scale),
+            _ptr(sub_rows, ctypes.c_int64), hi - lo,
+            _ptr(sub_o, ctypes.c_double), _ptr(sub_lse, ctypes.c_double))
+
+    if threads == 1:
+        statuses = [run(0)]
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as pool:
+            statuses = list(pool.map(run, range(threads)))
+    if any(s != 0 for s in statuses):
+        raise RuntimeError(f"oracle failed with status {statuses}")
+    return o, lse
+
+
+def attention(q, k, v, causal: bool, scale: float, threads: int = 1,
+              lib: ctypes.CDLL | None = None):
+    """Oracle output for every row: ``o`` float64 [B,H,N,d], ``lse`` float64 [B,H,N]."""
+    q, k, v = _check_inputs(q, k, v)
+    B, H, N, d = q.shape
+    o, lse = attention_rows(q, k, v, causal, scale, np.arange(B * H * N), threads, lib)
+    return o.reshape(B, H, N, d), lse.reshape(B, H, N)
