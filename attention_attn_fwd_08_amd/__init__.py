@@ -1,1 +1,134 @@
-"""MI355X-native fused attention forward (placeholder until the binding lands)."""
+"""MI355X-native fused attention forward: thin Python binding over the C ABI.
+
+Every step of the computation runs in the HIP library ``libattn_fwd.so``
+(built from ``csrc/attn_fwd.hip`` for gfx950).  This module only checks and
+marshals arguments: PyTorch supplies device memory and the current stream.
+There is no fallback: if the library is missing, calls raise.
+
+    o, lse = attn_fwd(q, k, v, causal=False, scale=None)
+
+computes o = softmax(scale * q k^T) v and lse = ln sum exp(scale * q k^T) per
+row, for bf16 tensors of shape [B, H, N, d] (the flash-attention forward of the
+ThunderKittens write-up, 88811315.cn, "H100 FlashAttention-2 forward example").
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+__all__ = ["attn_fwd", "attn_fwd_raw", "attn_fwd_strerror", "load_library", "LIBRARY",
+           "Status", "AttnError"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libattn_fwd.so")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class Status:
+    """Status codes of include/attn_fwd.h."""
+    OK = 0
+    ERR_NULL = 1
+    ERR_SHAPE = 2
+    ERR_HEAD_DIM = 3
+    ERR_SEQ_MULTIPLE = 4
+    ERR_ALIGN = 5
+    ERR_SCALE = 6
+    ERR_HIP = 7
+    ERR_DEVICE = 8
+
+
+class AttnError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"attn_fwd failed ({status}): {message}")
+        self.status = status
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load the HIP library (``libattn_fwd.so`` next to this file by default)."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIBRARY):
+                raise RuntimeError(
+                    f"{LIBRARY} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`"
+                    " or `python attention_attn_fwd_08_amd/_build.py`")
+            _lib = _declare(ctypes.CDLL(LIBRARY))
+    return _lib
+
+
+def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    vp = ctypes.c_void_p
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                             ctypes.c_int, ctypes.c_int, ctypes.c_float, vp]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_strerror.argtypes = [ctypes.c_int]
+    lib.attn_fwd_strerror.restype = ctypes.c_char_p
+    lib.attn_fwd_abi_version.argtypes = []
+    lib.attn_fwd_abi_version.restype = ctypes.c_int
+    return lib
+
+
+def attn_fwd_strerror(status: int) -> str:
+    return load_library().attn_fwd_strerror(int(status)).decode()
+
+
+def attn_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
+                 B: int, H: int, N: int, d: int, causal: bool, scale: float,
+                 stream: int = 0) -> int:
+    """Call the C entry point with raw integer addresses; returns the status."""
+    lib = load_library()
+    return lib.attn_fwd(q_ptr or None, k_ptr or None, v_ptr or None, o_ptr or None,
+                        lse_ptr or None, int(B), int(H), int(N), int(d), int(bool(causal)),
+                        float(scale), stream or None)
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """Fused attention forward on torch bf16 device tensors [B, H, N, d].
+
+    Returns ``(o, lse)``: ``o`` bf16 [B, H, N, d] and ``lse`` float32 [B, H, N].
+    ``out`` / ``lse`` may be given to write into existing tensors.  Runs
+    asynchronously on the current stream of ``q``'s device.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D tensor [B, H, N, d]")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k and v must have the same shape")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on the same device")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype != torch.bfloat16 or out.device != q.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q on q's device")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif (tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or lse.device != q.device
+          or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, N] on q's device")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        status = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), B, H, N, d, causal, scale, stream)
+    if status != Status.OK:
+        raise AttnError(status, attn_fwd_strerror(status))
+    return out, lse

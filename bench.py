@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Attention-forward throughput on one MI355X, with roofline and CPU baseline.
+
+One step = one call of the fused attention forward (every stage of the path:
+tile schedule, Q load, K/V streaming, both MFMA products, online softmax and
+the O/LSE epilogue) over one batch of seeded synthetic inputs that are already
+resident in HBM.  Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Throughput counts 4*B*H*N^2*d flops, halved for causal.  The kernel's own
+average duration comes from HIP events recorded around every launch on the
+stream the kernel runs on (torch's current stream, which the library is handed).
+The CPU baseline times the fp64 oracle on a bounded sample of query rows of
+the same workload on this host's cores, and reuses those oracle rows to check
+the benchmarked output.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from attention_attn_fwd_08_amd.inputs import HEADLINE, WORKLOADS, sample_rows, workload_inputs  # noqa: E402
+
+# MI355X published dense bf16 MFMA peak: 256 CUs x 4096 flop/clk/CU x 2.4 GHz.
+PEAK_BF16_TFLOPS = 2516.6
+KERNEL_SOURCE = os.path.join(ROOT, "attention_attn_fwd_08_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+O_MAX_TOL, O_MEAN_TOL, LSE_MAX_TOL = 2e-2, 2e-3, 1e-3
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none for this workload or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("workloads", {}).get(workload)
+    if not entry or rec.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, target_gflop: float, threads: int):
+    """Time the oracle on a bounded sample of rows; returns (record, rows, o, lse)."""
+    import numpy as np
+    import oracle
+    per_row_keys = (w.N + 1) / 2 if w.causal else w.N
+    per_row_flop = 4.0 * per_row_keys * w.d
+    n_heads = w.B * w.H
+    per_head = max(8, int(target_gflop * 1e9 / per_row_flop / n_heads))
+    per_head = min(per_head, w.N)
+    rows = sample_rows(w, per_head=per_head)
+    oracle.load()  # compile / load outside the timed region
+    t0 = time.perf_counter()
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, w.causal, w.scale, rows, threads=threads)
+    dt = time.perf_counter() - t0
+    i = rows % w.N
+    flop = float(np.sum(4.0 * ((i + 1) if w.causal else w.N) * w.d))
+    rec = {
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{rows.size} query rows of {w.name} ({per_head} per head, every head; "
+                   f"{flop / 1e9:.1f} GFLOP fp64) in {dt:.2f} s wall on {threads} threads"),
+    }
+    return rec, rows, o_ref, lse_ref
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-gflop", type=float, default=30.0,
+                    help="size of the oracle sample for the CPU baseline (fp64 GFLOP)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (for profiler runs)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build is a single-GPU kernel "
+              "(--gpus 1); multi-GPU runs are not supported.", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import attention_attn_fwd_08_amd as af
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[args.workload]
+    log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
+
+    t0 = time.perf_counter()
+    q_bits, k_bits, v_bits = workload_inputs(w)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    def dev_tensor(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = dev_tensor(q_bits), dev_tensor(k_bits), dev_tensor(v_bits)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        af.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_begin = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = (t_end - t_begin) * 1e3 / args.steps
+    kernel_ms = sum(launch_ms) / len(launch_ms)
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, kernel avg {kernel_ms:.4f} ms, "
+        f"min {min(launch_ms):.4f}, max {max(launch_ms):.4f}")
+
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+    traffic = measured_traffic(w.name)
+
+    result = {
+        "metric": "attention fwd TFLOP/s at 1 MI355X and % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+            "causal": w.causal, "scale": w.scale, "seed": w.seed,
+            "qk_sigma": w.qk_sigma, "v_sigma": w.v_sigma, "parallelism": "none",
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel_avg_ms": round(kernel_ms, 5),
+            "flop_per_launch": w.flops,
+            "algorithmic_hbm_bytes_per_launch": w.hbm_bytes,
+        },
+        "cpu_baseline": None,
+    }
+
+    ok = True
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        log(f"oracle sample on {threads} host threads ...")
+        rec, rows, o_ref, lse_ref = cpu_baseline(w, q_bits, k_bits, v_bits, args.cpu_gflop,
+                                                 threads)
+        result["cpu_baseline"] = rec
+        o_g = o.reshape(-1, w.d)[torch.from_numpy(rows).to(dev)].float().cpu().numpy()
+        l_g = lse.reshape(-1)[torch.from_numpy(rows).to(dev)].cpu().numpy()
+        eo = np.abs(o_g.astype(np.float64) - o_ref)
+        el = np.abs(l_g.astype(np.float64) - lse_ref)
+        parity = {"rows": int(rows.size), "o_max_err": float(eo.max()),
+                  "o_mean_err": float(eo.mean()), "lse_max_err": float(el.max())}
+        ok = (parity["o_max_err"] <= O_MAX_TOL and parity["o_mean_err"] <= O_MEAN_TOL
+              and parity["lse_max_err"] <= LSE_MAX_TOL)
+        parity["ok"] = ok
+        result["parity"] = parity
+        log(f"oracle: {rec['sample']}; parity {parity}")
+
+    print(json.dumps(result), flush=True)
+    return 0 if ok else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,92 @@
+/*
+ * attn_fwd.h -- C ABI of the MI355X (gfx950) fused attention forward library.
+ *
+ * The operation (flash-attention forward; ThunderKittens write-up,
+ * 88811315.cn, "RTX 4090 flash-attention example" and "H100 FlashAttention-2
+ * forward example"; the same kernels are summarised on GeekNews, "Ejemplo de
+ * FlashAttention y rendimiento"):
+ *
+ *   for every batch b < B, head h < H and query row i < N
+ *     s_ij   = scale * sum_t q[b,h,i,t] * k[b,h,j,t]        for visible j
+ *     o[b,h,i,:] = sum_j softmax_j(s_i.) * v[b,h,j,:]
+ *     lse[b,h,i] = ln sum_j exp(s_ij)                          (natural log)
+ *
+ * where the visible keys are all j < N, or j <= i when `causal` is non-zero
+ * (query i sees keys 0..i, diagonal included).  The N x N score matrix is
+ * never stored: keys and values are streamed in tiles and a running row
+ * maximum and normaliser are kept per query, the recurrence those examples
+ * print.  Inputs are bf16, products are accumulated in fp32, softmax runs in
+ * fp32, the probabilities are rounded to bf16 for the second product (as in
+ * those examples), O is rounded to bf16 (round-to-nearest-even) and the
+ * log-sum-exp is fp32.  The examples multiply Q by the temperature in bf16;
+ * this library applies `scale` to the fp32 scores instead.
+ *
+ * No HIP header is needed to call this library.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Every argument check runs before any HIP call; on an error
+ * return nothing has been launched and no output byte has been written. */
+enum attn_fwd_status {
+    ATTN_OK = 0,               /* launched (or nothing to do)                  */
+    ATTN_ERR_NULL = 1,         /* a pointer is NULL while B*H*N > 0            */
+    ATTN_ERR_SHAPE = 2,        /* B, H or N negative, or the sizes overflow    */
+    ATTN_ERR_HEAD_DIM = 3,     /* d is not 64 or 128                           */
+    ATTN_ERR_SEQ_MULTIPLE = 4, /* N is not a multiple of 128                   */
+    ATTN_ERR_ALIGN = 5,        /* a pointer is not 16-byte aligned             */
+    ATTN_ERR_SCALE = 6,        /* scale is not finite or not > 0               */
+    ATTN_ERR_HIP = 7,          /* the HIP runtime reported an error at launch  */
+    ATTN_ERR_DEVICE = 8        /* the current device is not a gfx950 GPU       */
+};
+
+/*
+ * attn_fwd -- enqueue the fused attention forward on `stream`.
+ *
+ *   q, k, v  device pointers to bf16 bit patterns, each [B, H, N, d]
+ *            contiguous row-major (d fastest), 16-byte aligned.  Read only.
+ *   o        device pointer, bf16 [B, H, N, d] contiguous, 16-byte aligned.
+ *            Written completely.
+ *   lse      device pointer, fp32 [B, H, N] contiguous, 16-byte aligned.
+ *            Written completely: natural-log log-sum-exp of each row's
+ *            scaled scores.  Required (not optional).
+ *   B, H, N  batch, heads, sequence length (queries = keys = N).  Any of them
+ *            may be 0 (nothing is launched).  N must be a multiple of 128.
+ *   d        head dimension: 64 or 128.
+ *   causal   0: every query sees every key.  Non-zero: query i sees keys
+ *            0..i (lower-triangular mask, top-left aligned).
+ *   scale    multiplies q.k; finite and > 0 (1/sqrt(d) is the usual value).
+ *   stream   a hipStream_t cast to void*; NULL means the default stream.
+ *
+ * Ownership: the caller owns every buffer; the library allocates no device
+ * memory and keeps no per-call state.  The only global state is a per-device
+ * cache of the device's properties, filled once.  Calls are re-entrant and
+ * may run concurrently on different streams.
+ *
+ * Semantics: asynchronous.  ATTN_OK means the kernel was enqueued; results
+ * are visible after the stream (or an event on it) is synchronised, and a
+ * fault during execution surfaces there, as with any HIP launch.  `o` and
+ * `lse` must not overlap q, k or v (not checked).  Non-finite input values
+ * give undefined (non-finite) outputs for the rows that see them.
+ */
+int attn_fwd(const void *q, const void *k, const void *v,
+             void *o, float *lse,
+             int B, int H, int N, int d,
+             int causal, float scale,
+             void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *attn_fwd_strerror(int status);
+
+/* ABI version of this header's entry points (currently 1). */
+int attn_fwd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

@@ -1,0 +1,117 @@
+"""The C ABI: the library loads, exports what include/attn_fwd.h declares, and
+rejects bad arguments before touching the GPU.
+
+Every call here fails validation (or is empty) by construction, so no HIP call
+is made and the fake addresses are never dereferenced; these tests run on a
+machine without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_attn_fwd_08_amd as af
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(af.LIBRARY):
+        from attention_attn_fwd_08_amd import _build
+        _build.build()
+    return af.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["attn_fwd", "attn_fwd_abi_version", "attn_fwd_strerror"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported"
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_codes_match_header(lib):
+    text = open(HEADER).read()
+    codes = dict((n, int(v)) for n, v in re.findall(r"ATTN_(\w+)\s*=\s*(\d+)", text))
+    for name, value in codes.items():
+        assert getattr(af.Status, name) == value
+        msg = af.attn_fwd_strerror(value)
+        assert msg and msg != "unknown status"
+    assert af.attn_fwd_strerror(12345) == "unknown status"
+    assert lib.attn_fwd_abi_version() == 1
+
+
+def call(B=2, H=3, N=256, d=128, causal=0, scale=0.088, q=FAKE, k=FAKE, v=FAKE, o=FAKE,
+         lse=FAKE):
+    return af.attn_fwd_raw(q, k, v, o, lse, B, H, N, d, causal, scale)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), af.Status.ERR_SHAPE),
+    (dict(H=-2), af.Status.ERR_SHAPE),
+    (dict(N=-128), af.Status.ERR_SHAPE),
+    (dict(d=32), af.Status.ERR_HEAD_DIM),
+    (dict(d=96), af.Status.ERR_HEAD_DIM),
+    (dict(d=0), af.Status.ERR_HEAD_DIM),
+    (dict(scale=0.0), af.Status.ERR_SCALE),
+    (dict(scale=-0.1), af.Status.ERR_SCALE),
+    (dict(scale=float("nan")), af.Status.ERR_SCALE),
+    (dict(scale=float("inf")), af.Status.ERR_SCALE),
+    (dict(N=100), af.Status.ERR_SEQ_MULTIPLE),
+    (dict(N=4097), af.Status.ERR_SEQ_MULTIPLE),
+    (dict(q=0), af.Status.ERR_NULL),
+    (dict(k=0), af.Status.ERR_NULL),
+    (dict(v=0), af.Status.ERR_NULL),
+    (dict(o=0), af.Status.ERR_NULL),
+    (dict(lse=0), af.Status.ERR_NULL),
+    (dict(q=FAKE + 8), af.Status.ERR_ALIGN),
+    (dict(k=FAKE + 2), af.Status.ERR_ALIGN),
+    (dict(v=FAKE + 4), af.Status.ERR_ALIGN),
+    (dict(o=FAKE + 1), af.Status.ERR_ALIGN),
+    (dict(lse=FAKE + 4), af.Status.ERR_ALIGN),
+    (dict(B=1 << 20, H=1 << 12, N=1 << 14), af.Status.ERR_SHAPE),
+    (dict(B=1, H=1, N=1 << 24, d=128), af.Status.ERR_SHAPE),
+])
+def test_rejects(lib, kw, status):
+    assert call(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0),
+                                dict(B=0, q=0, k=0, v=0, o=0, lse=0)])
+def test_empty_problem_is_a_noop(lib, kw):
+    assert call(**kw) == af.Status.OK
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        af.attn_fwd(x, x, x)
+    with pytest.raises(TypeError):
+        af.attn_fwd(x.float(), x, x)
+
+
+def test_no_undefined_kernel_stubs(lib):
+    """Every kernel launch stub is defined in the library (a host pass that
+    drops a kernel template leaves an undefined __device_stub__ symbol)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", af.LIBRARY], capture_output=True, text=True).stdout
+    undefined = [ln for ln in out.splitlines() if " U " in ln and "__device_stub__" in ln]
+    assert not undefined, undefined
