@@ -38,6 +38,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "attn_fwd.h"
 
 namespace {
@@ -65,18 +67,21 @@ constexpr float kRescaleLog2 = 8.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
-// LDS layouts.  A K or V stage is kBlockN rows of D bf16 (D*2 bytes), the
-// 16-byte chunks of each row permuted by an XOR with a function of the row.
+// LDS layouts.  A K or V stage is kBlockN rows of D bf16 (D*2 bytes); the
+// 16-byte chunks of each row are permuted by an XOR with a function of the
+// row, chosen against the way gfx950 services each read (measured with the
+// LDS bank-conflict counter: 16-byte reads are serviced 16 lanes at a time,
+// the 8-byte transposed reads 32 lanes at a time, 256 bytes per pass).
 //
-// K is read as the MFMA A operand: 32 lanes read the same chunk of 32
-// consecutive rows (16 bytes each).  XOR with row%16 (d=128) spreads any 16
-// consecutive rows over all 16 chunk positions of a 256-byte bank sweep.  For
-// d=64 a row is 128 bytes; the extra (row>>3)&1 term separates rows r and r+8.
+// K is read as the MFMA A operand: 16 lanes read the same chunk of 16
+// consecutive rows.  d=128: XOR with row%16 puts them in 16 distinct chunk
+// positions.  d=64 (128-byte rows, two rows per 256-byte pass): the 8 even
+// and the 8 odd rows of the 16 each land in distinct chunks.
 //
-// V is read with ds_read_b64_tr_b16: each 16-lane group reads 4 consecutive
-// rows x 32 contiguous bytes (a chunk pair).  The V function moves the chunk
-// pair of those 4 rows to 4 different places, and is still a permutation of
-// the chunks of any 16 consecutive rows.
+// V is read with ds_read_b64_tr_b16: 32 lanes read 4 consecutive rows x 2
+// adjacent 32-byte chunk pairs; the XOR moves the pair index by 2*(row%4) (+1
+// every 4 rows), so the 8 (row, pair) reads cover 8 distinct pair positions.
+// d=64: the two even (and two odd) rows of the 4 get pair offsets 0 and 2.
 template <int D>
 __device__ __forceinline__ int k_swz(int row) {
   if constexpr (D == 128) return row & 15;
@@ -84,18 +89,99 @@ __device__ __forceinline__ int k_swz(int row) {
 }
 template <int D>
 __device__ __forceinline__ int v_swz(int row) {
-  if constexpr (D == 128) return 2 * (row & 3) + 8 * ((row >> 2) & 1) + ((row >> 3) & 1);
-  else return 2 * (row & 3) + ((row >> 2) & 1);
+  if constexpr (D == 128) return 4 * (row & 3) + 2 * ((row >> 2) & 1);
+  else return 4 * ((row >> 1) & 1);
 }
 
-// 16 bytes global -> LDS without passing through registers: lane i of the
-// wave writes bytes [16i, 16i+16) after the wave-uniform LDS address `dst`.
-// (Only the device pass sees the builtin; the host pass, which compiles just
-// the launch stub, drops a kernel template that names it.)
-__device__ __forceinline__ void load16_to_lds(const void* src, unsigned char* dst) {
+// 16 bytes global -> LDS without passing through registers, through a buffer
+// resource (base, byte size): lane i of the wave reads bytes [voff+soff,
+// +16) of the buffer (reads past the size return zeros) and writes them to
+// LDS bytes [16i, 16i+16) after the wave-uniform address `dst`.  (Only the
+// device pass sees the builtins; the host pass, which compiles just the
+// launch stub, drops a kernel template that names them.)
+struct BufferRsrc {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+  __amdgpu_buffer_rsrc_t r;
 #endif
+};
+__device__ __forceinline__ BufferRsrc make_rsrc(const void* base, int bytes) {
+  BufferRsrc b;
+#if defined(__HIP_DEVICE_COMPILE__)
+  // Word 3 = 0x00020000: raw (untyped) 32-bit data for gfx9-family buffers.
+  b.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+#endif
+  return b;
+}
+__device__ __forceinline__ void load16_to_lds(const BufferRsrc& rsrc, int voff, int soff,
+                                              unsigned char* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc.r, (lds_void*)dst, 16, voff, soff, 0, 0);
+#endif
+}
+
+// max / sum of a value held by lanes L and L^32 (the two halves of one query).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Per-wave state and the steps of one 64-key tile.  The tile loop is software
+// pipelined: while the scores of tile t are turned into probabilities (VALU,
+// transcendental) the MFMA pipe computes the scores of tile t+1, and while
+// O^T += V_t^T P_t^T runs on the MFMA pipe the VALU reduces tile t+1's
+// scores to their row maximum.  K therefore runs one tile ahead of V.
+template <int D>
+struct Tile {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kSteps = D / 16;    // MFMA k-steps of one 32x32 score block
+  static constexpr int kDBlocks = D / 32;  // 32-row blocks of O^T
+  static constexpr int kStageBytes = kBlockN * kRowBytes;
+};
+
+// Scores S^T of the two 32-key blocks of a K stage against this wave's 32
+// queries.  Accumulator register r of lane L: key 8*(r/4) + 4*(L/32) + r%4 of
+// the block, query L%32.
+template <int D>
+__device__ __forceinline__ void scores(const unsigned char* k_lds, const int (&k_off)[Tile<D>::kSteps],
+                                       const bf16x8 (&qf)[Tile<D>::kSteps], f32x16 (&s)[2]) {
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
+#pragma unroll
+    for (int st = 0; st < Tile<D>::kSteps; ++st) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(k_lds + sb * 32 * Tile<D>::kRowBytes + k_off[st]);
+      s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[sb], 0, 0, 0);
+    }
+  }
+}
+
+// Causal mask of a tile whose keys start at key0, for queries starting at q0.
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int key0, int q0, int l32, int half) {
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kj = key0 + sb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (kj > q0 + l32) s[sb][r] = -INFINITY;
+    }
+}
+
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
+  float m0 = fmaxf(s[0][0], s[0][1]);
+  float m1 = fmaxf(s[1][0], s[1][1]);
+#pragma unroll
+  for (int r = 2; r < 16; ++r) {
+    m0 = fmaxf(m0, s[0][r]);
+    m1 = fmaxf(m1, s[1][r]);
+  }
+  return pair_max(fmaxf(m0, m1));
 }
 
 template <int D, bool CAUSAL>
@@ -103,16 +189,19 @@ __global__ __launch_bounds__(kThreads, 2)  // two waves per SIMD: <= 256 registe
 void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, __bf16* __restrict__ o,
                      float* __restrict__ lse, int N, float c) {
-  constexpr int kRowBytes = D * 2;
+  using T = Tile<D>;
+  constexpr int kRowBytes = T::kRowBytes;
   constexpr int kChunksPerRow = D / 8;
-  constexpr int kSteps = D / 16;                 // MFMA k-steps of one score block
-  constexpr int kDBlocks = D / 32;               // 32-row blocks of O^T
-  constexpr int kStageBytes = kBlockN * kRowBytes;
-  constexpr int kRowsPerLoad = kWave * 16 / kRowBytes;            // rows one wave load fills
+  constexpr int kSteps = T::kSteps;
+  constexpr int kDBlocks = T::kDBlocks;
+  constexpr int kStageBytes = T::kStageBytes;
+  constexpr int kRowsPerLoad = kWave * 16 / kRowBytes;              // rows one wave load fills
   constexpr int kLoadsPerWave = kBlockN / (kRowsPerLoad * kWaves);  // per tensor per stage
 
-  // [stage][K | V][kBlockN rows]
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * kStageBytes];
+  // K stages 0,1 then V stages 0,1.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * kStageBytes];
+  unsigned char* const k_base = smem;
+  unsigned char* const v_base = smem + 2 * kStageBytes;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -138,26 +227,42 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const __bf16* const vh = v + head_off;
   const int q0 = qt * kBlockM + wave * kQueriesPerWave;  // this wave's first query
 
-  // Global -> LDS copy of one K and one V stage.  Lane i of a wave load fills
+  // Global -> LDS copy of one K or V stage.  Lane i of a wave load fills
   // bytes [16i, 16i+16) after the wave's base: row base+i/kChunksPerRow,
   // physical chunk i%kChunksPerRow, which holds logical chunk (that ^ swz).
+  // The lane's byte offset within a tile is fixed; the tile adds a scalar.
+  const BufferRsrc k_rsrc = make_rsrc(kh, N * kRowBytes);
+  const BufferRsrc v_rsrc = make_rsrc(vh, N * kRowBytes);
   const int ld_row = lane / kChunksPerRow;
   const int ld_chunk = lane % kChunksPerRow;
-  auto load_stage = [&](int kt0, int stage) {
+  int k_ld_off[kLoadsPerWave], v_ld_off[kLoadsPerWave];
 #pragma unroll
-    for (int it = 0; it < kLoadsPerWave; ++it) {
-      const int row0 = (wave * kLoadsPerWave + it) * kRowsPerLoad;
-      const int row = row0 + ld_row;
-      const size_t g = (size_t)(kt0 + row) * D;
-      unsigned char* kdst = smem + (2 * stage) * kStageBytes + row0 * kRowBytes;
-      unsigned char* vdst = smem + (2 * stage + 1) * kStageBytes + row0 * kRowBytes;
-      load16_to_lds(kh + g + (ld_chunk ^ k_swz<D>(row)) * 8, kdst);
-      load16_to_lds(vh + g + (ld_chunk ^ v_swz<D>(row)) * 8, vdst);
-    }
+  for (int it = 0; it < kLoadsPerWave; ++it) {
+    const int row = (wave * kLoadsPerWave + it) * kRowsPerLoad + ld_row;
+    k_ld_off[it] = row * kRowBytes + ((ld_chunk ^ k_swz<D>(row)) << 4);
+    v_ld_off[it] = row * kRowBytes + ((ld_chunk ^ v_swz<D>(row)) << 4);
+  }
+  auto load_k = [&](int tile, int stage) {
+#pragma unroll
+    for (int it = 0; it < kLoadsPerWave; ++it)
+      load16_to_lds(k_rsrc, k_ld_off[it], tile * kStageBytes,
+                    k_base + stage * kStageBytes + (wave * kLoadsPerWave + it) * kRowsPerLoad * kRowBytes);
+  };
+  auto load_v = [&](int tile, int stage) {
+#pragma unroll
+    for (int it = 0; it < kLoadsPerWave; ++it)
+      load16_to_lds(v_rsrc, v_ld_off[it], tile * kStageBytes,
+                    v_base + stage * kStageBytes + (wave * kLoadsPerWave + it) * kRowsPerLoad * kRowBytes);
   };
 
+  // Tiles this workgroup visits; causal tiles from first_diag on straddle the
+  // diagonal of at least one of its waves and are masked.
   const int n_tiles = (CAUSAL ? (qt + 1) * kBlockM : N) / kBlockN;
-  load_stage(0, 0);
+  const int first_diag = CAUSAL ? qt * (kBlockM / kBlockN) : n_tiles;
+
+  load_k(0, 0);
+  load_v(0, 0);
+  if (n_tiles > 1) load_k(1, 1);
 
   // Q^T as MFMA B operand: lane L holds query q0+L%32, features 8*(L/32)..+7
   // of each 16-feature step.  Loaded once per tile.
@@ -165,74 +270,96 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   {
     const __bf16* qrow = qh + (size_t)(q0 + l32) * D + 8 * half;
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
+    for (int st = 0; st < kSteps; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st);
   }
 
-  // Per-lane LDS byte offsets (stage-relative) of the MFMA operand reads.
-  // K: row sb*32 + L%32, logical chunk 2*st + L/32.
-  // V (transposed reads): 16-lane group G = L/16 and s = L%16 read row
-  // 16*cc + 4*(G/2) + s/4 (+8 for the second read) and features
-  // 32*b + 16*(G%2) + 4*(s%4) .. +3; lane L then holds feature 32*b + L%32 of
-  // keys 16cc + 4*(L/32) + 0..3 (first read) and 16cc + 8 + 4*(L/32) + 0..3
-  // (second read): the order the P^T registers use.
+  // Per-lane LDS byte offsets (stage-relative) of the operand reads.
+  // K (A operand of S^T): row L%32 (+32 per block), logical chunk 2*st + L/32.
+  int k_off[kSteps];
+#pragma unroll
+  for (int st = 0; st < kSteps; ++st)
+    k_off[st] = l32 * kRowBytes + (((2 * st + half) ^ k_swz<D>(l32)) << 4);
+  // V (A operand of O^T, transposed reads): 16-lane group G = L/16 and
+  // s = L%16 read row 16*cc + 4*(G/2) + s/4 (+8 for the second read) and
+  // features 32*b + 16*(G%2) + 4*(s%4) .. +3; lane L then holds feature
+  // 32*b + L%32 of keys 16cc + 4*(L/32) + 0..3 (first read) and
+  // 16cc + 8 + 4*(L/32) + 0..3 (second read), the key order of P^T's slots.
+  // The swizzle depends on row%16 only, identical for every (sb, cc), and the
+  // d-block b only flips bits 6-7 of the offset (chunk bits 2-3).
   const int g16 = lane >> 4;
   const int s16 = lane & 15;
-  const int v_row = 4 * (g16 >> 1) + (s16 >> 2);  // < 8; the second read adds 8
-  const int v_col = 16 * (g16 & 1) + 4 * (s16 & 3);
+  int v_off[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 4 * (g16 >> 1) + (s16 >> 2) + 8 * h;
+    const int col = 16 * (g16 & 1) + 4 * (s16 & 3);
+    v_off[h] = r * kRowBytes + (((col >> 3) ^ v_swz<D>(r)) << 4) + (col & 7) * 2;
+  }
 
   f32x16 acc[kDBlocks];
 #pragma unroll
   for (int b = 0; b < kDBlocks; ++b)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
-  float m_ref = -INFINITY;  // reference maximum (raw score units) for query q0+L%32
-  float l_run = 0.f;        // this lane's half of the normaliser
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int stage = t & 1;
-    const int kt0 = t * kBlockN;
-    __syncthreads();  // stage `stage` has landed; stage^1 is free again
-    if (t + 1 < n_tiles) load_stage(kt0 + kBlockN, stage ^ 1);
-    const unsigned char* const k_lds = smem + (2 * stage) * kStageBytes;
-    const unsigned char* const v_lds = smem + (2 * stage + 1) * kStageBytes;
+  __syncthreads();  // K0, V0, K1 have landed
 
+  // Prologue: scores of tile 0 and the first reference maximum.  Tile 0
+  // holds key 0, which every query sees, so the maximum is finite.
+  f32x16 s_a[2], s_b[2];
+  scores<D>(k_base, k_off, qf, s_a);
+  if (CAUSAL && first_diag == 0) mask_tile(s_a, 0, q0, l32, half);
+  float m_ref = tile_max(s_a);  // reference maximum (raw score units), query q0+L%32
+  float l_run = 0.f;            // this lane's half of the normaliser
+
+  // One tile: s_cur holds tile t's (masked) scores, s_next receives tile
+  // t+1's.  HAS_NEXT and MASK_NEXT are compile-time so the body is straight
+  // line code the scheduler can interleave (MFMA of one phase against VALU).
+  auto step = [&](auto has_next_tag, auto mask_next_tag, int t, f32x16(&s_cur)[2],
+                  f32x16(&s_next)[2]) __attribute__((always_inline)) {
+    constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
+    constexpr bool MASK_NEXT = decltype(mask_next_tag)::value;
+    __syncthreads();  // K_{t+1} and V_t have landed; K_t and V_{t-1} are free
+    if (t + 2 < n_tiles) load_k(t + 2, t & 1);
+    if (HAS_NEXT) load_v(t + 1, (t + 1) & 1);
+
+    // Phase A: probabilities of tile t (VALU) while S_{t+1} runs on MFMA.
+    if constexpr (HAS_NEXT) scores<D>(k_base + ((t + 1) & 1) * kStageBytes, k_off, qf, s_next);
+    const float mc = m_ref * c;
+    bf16x8 pb[2][2];
 #pragma unroll
-    for (int sb = 0; sb < kBlockN / 32; ++sb) {
-      const int key0 = kt0 + sb * 32;
-      if (CAUSAL && key0 > q0 + kQueriesPerWave - 1) continue;  // wave-uniform
-
-      // S^T block: 32 keys x 32 queries.
-      f32x16 s = {};
-      {
-        const int row = sb * 32 + l32;
-        const unsigned char* krow = k_lds + row * kRowBytes;
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int st = 0; st < kSteps; ++st) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-              krow + (((2 * st + half) ^ k_swz<D>(row)) << 4));
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s, 0, 0, 0);
+      for (int cc = 0; cc < 2; ++cc) {
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          p[j] = __builtin_amdgcn_exp2f(fmaf(s_cur[sb][8 * cc + j], c, -mc));
+          pb[sb][cc][j] = (__bf16)p[j];
         }
+        l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       }
 
-      // Accumulator layout: register r of lane L is key 8*(r/4) + 4*(L/32) + r%4
-      // of the block, query L%32.
-      if (CAUSAL && key0 == q0) {
+    // Phase B: O^T += V_t^T P_t^T on MFMA while the VALU reduces S_{t+1}.
+    const unsigned char* const v_lds = v_base + (t & 1) * kStageBytes;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kj = 8 * (r >> 2) + 4 * half + (r & 3);
-          if (kj > l32) s[r] = -INFINITY;
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int b = 0; b < kDBlocks; ++b)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const unsigned char* a = v_lds + (sb * 32 + cc * 16) * kRowBytes;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + (v_off[0] ^ (b << 6))));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + (v_off[1] ^ (b << 6))));
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[sb][cc], acc[b], 0, 0, 0);
         }
-      }
-
-      float mx = fmaxf(s[0], s[1]);
-#pragma unroll
-      for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // Lanes L and L^32 hold the same query and agree on every value below.
-      // The first block a wave sees holds key 0, so mx is finite there and
-      // m_ref becomes finite at once.
+    if constexpr (HAS_NEXT) {
+      if constexpr (MASK_NEXT) mask_tile(s_next, (t + 1) * kBlockN, q0, l32, half);
+      const float mx = tile_max(s_next);
+      // Lazy rescale: lanes L and L^32 agree on mx and m_ref, hence on `grow`.
       const bool grow = (mx - m_ref) * c > kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform, rare after the first block
+      if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform and rare
         const float m_new = grow ? mx : m_ref;
         const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c);
         l_run *= alpha;
@@ -242,47 +369,39 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
         m_ref = m_new;
       }
-      const float mc = m_ref * c;
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -mc));
-        l_run += p[r];
-      }
+    }
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
+  auto copy_scores = [](f32x16(&dst)[2], const f32x16(&src)[2]) __attribute__((always_inline)) {
+    dst[0] = src[0];
+    dst[1] = src[1];
+  };
 
-      // P^T as B operand: 16-key step cc uses registers 8cc..8cc+7, i.e. keys
-      // 16cc + 8*(j/4) + 4*(L/32) + j%4 for slot j.
-      bf16x8 pb[2];
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pb[cc][j] = (__bf16)p[8 * cc + j];
-
-      // V^T as A operand with the same key order, via transposed LDS reads.
-#pragma unroll
-      for (int b = 0; b < kDBlocks; ++b) {
-        const int col = 32 * b + v_col;
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const int r1 = sb * 32 + 16 * cc + v_row;
-          const int r2 = r1 + 8;
-          const unsigned char* a1 =
-              v_lds + r1 * kRowBytes + (((col >> 3) ^ v_swz<D>(r1)) << 4) + (col & 7) * 2;
-          const unsigned char* a2 =
-              v_lds + r2 * kRowBytes + (((col >> 3) ^ v_swz<D>(r2)) << 4) + (col & 7) * 2;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a1);
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a2);
-          const bf16x4 lob = __builtin_bit_cast(bf16x4, lo);
-          const bf16x4 hib = __builtin_bit_cast(bf16x4, hi);
-          const bf16x8 vf = {lob[0], lob[1], lob[2], lob[3], hib[0], hib[1], hib[2], hib[3]};
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[cc], acc[b], 0, 0, 0);
-        }
-      }
+  // Steps whose successor tile needs no mask run in pairs, so the two score
+  // buffers alternate without copies.  Causal workgroups end with the two
+  // tiles on their diagonal: the steps before them mask their successor.
+  const int n_plain = CAUSAL ? (n_tiles >= 3 ? n_tiles - 3 : 0) : n_tiles - 1;
+  int t = 0;
+  for (; t + 1 < n_plain; t += 2) {
+    step(yes{}, no{}, t, s_a, s_b);
+    step(yes{}, no{}, t + 1, s_b, s_a);
+  }
+  if (t < n_plain) {
+    step(yes{}, no{}, t, s_a, s_b);
+    copy_scores(s_a, s_b);
+    ++t;
+  }
+  if constexpr (CAUSAL) {
+    for (; t + 1 < n_tiles; ++t) {
+      step(yes{}, yes{}, t, s_a, s_b);
+      copy_scores(s_a, s_b);
     }
   }
+  step(no{}, no{}, t, s_a, s_b);  // the last tile has no successor
 
   // Epilogue: O = acc / l, rounded to bf16; lse = (m*c + log2 l) * ln 2.
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   const float inv = 1.0f / l_tot;
   __bf16* const orow = o + head_off + (size_t)(q0 + l32) * D;
 #pragma unroll
@@ -344,7 +463,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   const int64_t bh = (int64_t)B * H;
   if (bh > INT32_MAX) return ATTN_ERR_SHAPE;
   if (bh * (N / kBlockM) > INT32_MAX) return ATTN_ERR_SHAPE;  // grid size
-  if ((int64_t)N * d > INT32_MAX) return ATTN_ERR_SHAPE;
+  if ((int64_t)N * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;  // one head's bytes fit an int
   if (bh == 0 || N == 0) return ATTN_OK;
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))

@@ -74,8 +74,8 @@ def cpu_baseline(w, q, k, v, target_gflop: float, threads: int):
     t0 = time.perf_counter()
     o_ref, lse_ref = oracle.attention_rows(q, k, v, w.causal, w.scale, rows, threads=threads)
     dt = time.perf_counter() - t0
-    i = rows % w.N
-    flop = float(np.sum(4.0 * ((i + 1) if w.causal else w.N) * w.d))
+    visible = (rows % w.N) + 1 if w.causal else np.full(rows.size, w.N)
+    flop = float(np.sum(4.0 * visible * w.d))
     rec = {
         "value": flop / dt / 1e12,
         "unit": "TFLOP/s",
@@ -93,10 +93,13 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-gflop", type=float, default=30.0,
+    ap.add_argument("--cpu-gflop", type=float, default=80.0,
                     help="size of the oracle sample for the CPU baseline (fp64 GFLOP)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (for profiler runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB, 3 times (the "
+                         "known-size reference that scales the HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -117,6 +120,15 @@ def main() -> int:
         return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes 3 times")
+        return 0
     w = WORKLOADS[args.workload]
     log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
 

@@ -84,6 +84,8 @@ def call(B=2, H=3, N=256, d=128, causal=0, scale=0.088, q=FAKE, k=FAKE, v=FAKE, 
     (dict(lse=FAKE + 4), af.Status.ERR_ALIGN),
     (dict(B=1 << 20, H=1 << 12, N=1 << 14), af.Status.ERR_SHAPE),
     (dict(B=1, H=1, N=1 << 24, d=128), af.Status.ERR_SHAPE),
+    (dict(B=1, H=1, N=1 << 23, d=128), af.Status.ERR_SHAPE),
+    (dict(B=1, H=1, N=1 << 24, d=64), af.Status.ERR_SHAPE),
 ])
 def test_rejects(lib, kw, status):
     assert call(**kw) == status
