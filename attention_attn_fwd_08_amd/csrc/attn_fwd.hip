@@ -8,25 +8,34 @@
 // and normaliser l so the N x N matrix never exists.
 //
 // Mapping to CDNA4 (not to the examples' warp/warpgroup design):
-//   * one workgroup = 4 waves of 64 lanes; each wave owns 32 queries;
+//   * a workgroup is 4 waves of 64 lanes owning 128 queries (32 per wave), and
+//     each SIMD runs two such waves (two workgroups per CU): the MFMA pipe
+//     of one wave overlaps the softmax VALU work of the other;
 //   * scores are formed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand, Q^T (held in
-//     registers for the whole tile) the B operand.  In the 32x32 accumulator
-//     lane L holds query L%32 and 16 of the 32 keys; lane L^32 holds the other
-//     16.  Row max / row sum are therefore in-lane plus one exchange with
-//     lane L^32, and the per-query rescale factor is a per-lane scalar;
+//     registers for the whole workgroup) the B operand.  In the 32x32
+//     accumulator lane L holds query L%32 and 16 of the 32 keys; lane L^32
+//     holds the other 16.  Row max / row sum are in-lane plus one
+//     v_permlane32_swap, and the per-query rescale factor is a per-lane scalar;
 //   * the probabilities P^T stay in registers: the accumulator of S^T,
 //     rounded to bf16, is directly the B operand of O^T += V^T P^T.  The key
-//     order inside each 16-key step is permuted the same way in V^T, which the
-//     contraction does not see;
+//     order inside each 16-key step is permuted the same way in V^T (read with
+//     ds_read_b64_tr_b16), which the contraction does not see;
 //   * softmax uses exp2 with log2(e) folded into the scale: p = 2^(s*c - m*c)
-//     with c = scale*log2(e), and lse = (m*c + log2 l) * ln 2;
-//   * K and V tiles move global -> LDS as 16-byte loads with an XOR-swizzled
-//     row layout so the 32 rows an MFMA operand read touches fall in distinct
-//     banks;
+//     with c = scale*log2(e), and lse = (m*c + log2 l) * ln 2.  O is rescaled
+//     only when a running maximum grows by more than 2^8 (rare after the
+//     first tile), otherwise the stale reference maximum is kept;
+//   * the 64-key tile loop is software pipelined: while the scores of tile t
+//     become probabilities (VALU) the MFMA pipe computes the scores of tile
+//     t+1, and while O^T += V_t^T P_t^T runs the VALU reduces tile t+1 to its
+//     row maxima; K therefore runs one tile ahead of V;
+//   * K and V tiles stream global -> LDS with buffer loads that write LDS
+//     directly (no register staging), double-buffered, with XOR swizzles
+//     that make every operand read bank-conflict free;
 //   * causal: key tiles past the workgroup's last query are never loaded,
-//     score blocks past a wave's last query are skipped, and only blocks on the
-//     diagonal are masked;
+//     and only the two tiles on the workgroup's diagonal are masked;
+//   * any N: a partial last query tile reads clamped Q rows and stores only
+//     rows < N; keys >= N read as zeros and are masked in the last key tile;
 //   * workgroup ids are remapped so that tiles of one head run on one XCD
 //     (workgroups are dispatched round-robin over the 8 XCDs), keeping that
 //     head's K/V in the XCD's L2; causal tiles of a head run longest first.
@@ -47,8 +56,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWave = 64;
@@ -57,7 +66,6 @@ constexpr int kThreads = kWave * kWaves;
 constexpr int kQueriesPerWave = 32;
 constexpr int kBlockM = kWaves * kQueriesPerWave;  // queries per workgroup
 constexpr int kBlockN = 64;                        // keys per LDS stage
-constexpr int kSeqMultiple = kBlockM;
 constexpr int kXcds = 8;
 // O is rescaled only when a query's block maximum exceeds the reference
 // maximum by more than this many powers of two; until then probabilities are
@@ -94,29 +102,31 @@ __device__ __forceinline__ int v_swz(int row) {
 }
 
 // 16 bytes global -> LDS without passing through registers, through a buffer
-// resource (base, byte size): lane i of the wave reads bytes [voff+soff,
-// +16) of the buffer (reads past the size return zeros) and writes them to
-// LDS bytes [16i, 16i+16) after the wave-uniform address `dst`.  (Only the
-// device pass sees the builtins; the host pass, which compiles just the
-// launch stub, drops a kernel template that names them.)
-struct BufferRsrc {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __amdgpu_buffer_rsrc_t r;
-#endif
-};
-__device__ __forceinline__ BufferRsrc make_rsrc(const void* base, int bytes) {
-  BufferRsrc b;
-#if defined(__HIP_DEVICE_COMPILE__)
+// resource {base, byte size}: lane i of the wave reads bytes [voff, voff+16)
+// of the buffer (offsets past the size, which the hardware range-checks,
+// return zeros) and
+// writes them to LDS bytes [16i, 16i+16) after the wave-uniform LDS byte
+// address `lds_addr` (set through M0).  Issued as inline assembly so the compiler does
+// not wait for these loads before unrelated LDS reads; the kernel waits for
+// them itself (wait_lds_dma) before the barrier that publishes them.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
   // Word 3 = 0x00020000: raw (untyped) 32-bit data for gfx9-family buffers.
-  b.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-#endif
-  return b;
+  return i32x4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes, 0x00020000};
 }
-__device__ __forceinline__ void load16_to_lds(const BufferRsrc& rsrc, int voff, int soff,
-                                              unsigned char* dst) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc.r, (lds_void*)dst, 16, voff, soff, 0, 0);
-#endif
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load16_to_lds(i32x4 rsrc, int voff, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// Wait until at most N of this wave's LDS-bound loads are still in flight.
+template <int N>
+__device__ __forceinline__ void wait_lds_dma() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // max / sum of a value held by lanes L and L^32 (the two halves of one query).
@@ -162,15 +172,19 @@ __device__ __forceinline__ void scores(const unsigned char* k_lds, const int (&k
   }
 }
 
-// Causal mask of a tile whose keys start at key0, for queries starting at q0.
-__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int key0, int q0, int l32, int half) {
+// Mask of a tile whose keys start at key0 for the queries q0 + L%32: a key is
+// visible iff key < N and, when causal, key <= query.
+template <bool CAUSAL>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int key0, int q0, int N, int l32,
+                                          int half) {
+  const int last = CAUSAL ? min(q0 + l32, N - 1) : N - 1;  // last visible key
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
+  for (int sb = 0; sb < 2; ++sb) {
+    const int lim = last - key0 - sb * 32 - 4 * half;  // visible iff in-block offset <= lim
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kj = key0 + sb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-      if (kj > q0 + l32) s[sb][r] = -INFINITY;
-    }
+    for (int r = 0; r < 16; ++r)
+      if (8 * (r >> 2) + (r & 3) > lim) s[sb][r] = -INFINITY;
+  }
 }
 
 __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
@@ -205,7 +219,7 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
@@ -214,7 +228,7 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // and consecutive logical ids walk the query tiles of one head, so the
   // workgroups resident on an XCD share one head's K/V in that XCD's L2.
   // Causal tiles of a head run longest first, so each XCD ends on short ones.
-  const int n_qt = N / kBlockM;
+  const int n_qt = (N + kBlockM - 1) / kBlockM;
   const int grid = gridDim.x;
   int lid = blockIdx.x;
   if (grid % kXcds == 0) lid = (lid % kXcds) * (grid / kXcds) + lid / kXcds;
@@ -227,12 +241,18 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const __bf16* const vh = v + head_off;
   const int q0 = qt * kBlockM + wave * kQueriesPerWave;  // this wave's first query
 
-  // Global -> LDS copy of one K or V stage.  Lane i of a wave load fills
+  // Tiles this workgroup visits; tiles from first_mask on are masked:
+  // causal, the tiles on the diagonal of at least one of its waves; else
+  // only a last tile that runs past N.
+  const int kv_end = CAUSAL ? min((qt + 1) * kBlockM, N) : N;
+  const int n_tiles = (kv_end + kBlockN - 1) / kBlockN;
+  const int first_mask = CAUSAL ? qt * (kBlockM / kBlockN)
+                                : (N % kBlockN ? n_tiles - 1 : n_tiles);
+
+  // Global -> LDS copy of one K or V tile.  Lane i of a wave load fills
   // bytes [16i, 16i+16) after the wave's base: row base+i/kChunksPerRow,
   // physical chunk i%kChunksPerRow, which holds logical chunk (that ^ swz).
-  // The lane's byte offset within a tile is fixed; the tile adds a scalar.
-  const BufferRsrc k_rsrc = make_rsrc(kh, N * kRowBytes);
-  const BufferRsrc v_rsrc = make_rsrc(vh, N * kRowBytes);
+  // The buffer starts at the tile, so rows past N fall outside its size.
   const int ld_row = lane / kChunksPerRow;
   const int ld_chunk = lane % kChunksPerRow;
   int k_ld_off[kLoadsPerWave], v_ld_off[kLoadsPerWave];
@@ -242,23 +262,22 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     k_ld_off[it] = row * kRowBytes + ((ld_chunk ^ k_swz<D>(row)) << 4);
     v_ld_off[it] = row * kRowBytes + ((ld_chunk ^ v_swz<D>(row)) << 4);
   }
-  auto load_k = [&](int tile, int stage) {
+  const unsigned lds_wave = (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)smem +
+                            wave * kLoadsPerWave * kRowsPerLoad * kRowBytes;
+  auto load_tile = [&](const __bf16* base, const int (&ld_off)[kLoadsPerWave], int region,
+                       int tile, int stage) __attribute__((always_inline)) {
+    const i32x4 rsrc = make_rsrc(base + (size_t)tile * kBlockN * D, (N - tile * kBlockN) * kRowBytes);
+    const unsigned dst = lds_wave + (2 * region + stage) * kStageBytes;
 #pragma unroll
     for (int it = 0; it < kLoadsPerWave; ++it)
-      load16_to_lds(k_rsrc, k_ld_off[it], tile * kStageBytes,
-                    k_base + stage * kStageBytes + (wave * kLoadsPerWave + it) * kRowsPerLoad * kRowBytes);
+      load16_to_lds(rsrc, ld_off[it], dst + it * kRowsPerLoad * kRowBytes);
   };
-  auto load_v = [&](int tile, int stage) {
-#pragma unroll
-    for (int it = 0; it < kLoadsPerWave; ++it)
-      load16_to_lds(v_rsrc, v_ld_off[it], tile * kStageBytes,
-                    v_base + stage * kStageBytes + (wave * kLoadsPerWave + it) * kRowsPerLoad * kRowBytes);
+  auto load_k = [&](int tile, int stage) __attribute__((always_inline)) {
+    load_tile(kh, k_ld_off, 0, tile, stage);
   };
-
-  // Tiles this workgroup visits; causal tiles from first_diag on straddle the
-  // diagonal of at least one of its waves and are masked.
-  const int n_tiles = (CAUSAL ? (qt + 1) * kBlockM : N) / kBlockN;
-  const int first_diag = CAUSAL ? qt * (kBlockM / kBlockN) : n_tiles;
+  auto load_v = [&](int tile, int stage) __attribute__((always_inline)) {
+    load_tile(vh, v_ld_off, 1, tile, stage);
+  };
 
   load_k(0, 0);
   load_v(0, 0);
@@ -268,7 +287,8 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // of each 16-feature step.  Loaded once per tile.
   bf16x8 qf[kSteps];
   {
-    const __bf16* qrow = qh + (size_t)(q0 + l32) * D + 8 * half;
+    const int row = min(q0 + l32, N - 1);  // rows past N: any valid row
+    const __bf16* qrow = qh + (size_t)row * D + 8 * half;
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st);
   }
@@ -302,13 +322,14 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
 
+  wait_lds_dma<0>();
   __syncthreads();  // K0, V0, K1 have landed
 
   // Prologue: scores of tile 0 and the first reference maximum.  Tile 0
   // holds key 0, which every query sees, so the maximum is finite.
   f32x16 s_a[2], s_b[2];
   scores<D>(k_base, k_off, qf, s_a);
-  if (CAUSAL && first_diag == 0) mask_tile(s_a, 0, q0, l32, half);
+  if (first_mask == 0) mask_tile<CAUSAL>(s_a, 0, q0, N, l32, half);
   float m_ref = tile_max(s_a);  // reference maximum (raw score units), query q0+L%32
   float l_run = 0.f;            // this lane's half of the normaliser
 
@@ -319,6 +340,7 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                   f32x16(&s_next)[2]) __attribute__((always_inline)) {
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
     constexpr bool MASK_NEXT = decltype(mask_next_tag)::value;
+    wait_lds_dma<0>();
     __syncthreads();  // K_{t+1} and V_t have landed; K_t and V_{t-1} are free
     if (t + 2 < n_tiles) load_k(t + 2, t & 1);
     if (HAS_NEXT) load_v(t + 1, (t + 1) & 1);
@@ -355,7 +377,7 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[sb][cc], acc[b], 0, 0, 0);
         }
     if constexpr (HAS_NEXT) {
-      if constexpr (MASK_NEXT) mask_tile(s_next, (t + 1) * kBlockN, q0, l32, half);
+      if constexpr (MASK_NEXT) mask_tile<CAUSAL>(s_next, (t + 1) * kBlockN, q0, N, l32, half);
       const float mx = tile_max(s_next);
       // Lazy rescale: lanes L and L^32 agree on mx and m_ref, hence on `grow`.
       const bool grow = (mx - m_ref) * c > kRescaleLog2;
@@ -379,9 +401,9 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   };
 
   // Steps whose successor tile needs no mask run in pairs, so the two score
-  // buffers alternate without copies.  Causal workgroups end with the two
-  // tiles on their diagonal: the steps before them mask their successor.
-  const int n_plain = CAUSAL ? (n_tiles >= 3 ? n_tiles - 3 : 0) : n_tiles - 1;
+  // buffers alternate without copies; the steps from first_mask-1 on mask
+  // their successor.
+  const int n_plain = first_mask - 1 > 0 ? first_mask - 1 : 0;
   int t = 0;
   for (; t + 1 < n_plain; t += 2) {
     step(yes{}, no{}, t, s_a, s_b);
@@ -392,15 +414,14 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     copy_scores(s_a, s_b);
     ++t;
   }
-  if constexpr (CAUSAL) {
-    for (; t + 1 < n_tiles; ++t) {
-      step(yes{}, yes{}, t, s_a, s_b);
-      copy_scores(s_a, s_b);
-    }
+  for (; t + 1 < n_tiles; ++t) {
+    step(yes{}, yes{}, t, s_a, s_b);
+    copy_scores(s_a, s_b);
   }
   step(no{}, no{}, t, s_a, s_b);  // the last tile has no successor
 
   // Epilogue: O = acc / l, rounded to bf16; lse = (m*c + log2 l) * ln 2.
+  if (q0 + l32 >= N) return;  // a partial last query tile stores only rows < N
   const float l_tot = pair_sum(l_run);
   const float inv = 1.0f / l_tot;
   __bf16* const orow = o + head_off + (size_t)(q0 + l32) * D;
@@ -444,7 +465,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 template <int D, bool CAUSAL>
 int launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
            float c, hipStream_t stream) {
-  const int n_qt = N / kBlockM;
+  const int n_qt = (N + kBlockM - 1) / kBlockM;
   const int grid = n_qt * BH;
   hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream,
                      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
@@ -459,10 +480,9 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   if (B < 0 || H < 0 || N < 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
   if (!(scale > 0.0f) || !isfinite(scale)) return ATTN_ERR_SCALE;
-  if (N % kSeqMultiple != 0) return ATTN_ERR_SEQ_MULTIPLE;
   const int64_t bh = (int64_t)B * H;
   if (bh > INT32_MAX) return ATTN_ERR_SHAPE;
-  if (bh * (N / kBlockM) > INT32_MAX) return ATTN_ERR_SHAPE;  // grid size
+  if (bh * (((int64_t)N + kBlockM - 1) / kBlockM) > INT32_MAX) return ATTN_ERR_SHAPE;  // grid
   if ((int64_t)N * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;  // one head's bytes fit an int
   if (bh == 0 || N == 0) return ATTN_OK;
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
@@ -491,7 +511,7 @@ extern "C" const char* attn_fwd_strerror(int status) {
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "B, H or N is negative, or the problem size overflows";
     case ATTN_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
-    case ATTN_ERR_SEQ_MULTIPLE: return "sequence length N must be a multiple of 128";
+    case ATTN_ERR_SEQ_MULTIPLE: return "reserved (any sequence length is accepted)";
     case ATTN_ERR_ALIGN: return "q, k, v, o and lse must be 16-byte aligned";
     case ATTN_ERR_SCALE: return "scale must be finite and greater than 0";
     case ATTN_ERR_HIP: return "the HIP runtime reported an error";

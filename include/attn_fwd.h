@@ -37,7 +37,7 @@ enum attn_fwd_status {
     ATTN_ERR_NULL = 1,         /* a pointer is NULL while B*H*N > 0            */
     ATTN_ERR_SHAPE = 2,        /* B, H or N negative, or the sizes overflow    */
     ATTN_ERR_HEAD_DIM = 3,     /* d is not 64 or 128                           */
-    ATTN_ERR_SEQ_MULTIPLE = 4, /* N is not a multiple of 128                   */
+    ATTN_ERR_SEQ_MULTIPLE = 4, /* reserved: any N >= 0 is accepted             */
     ATTN_ERR_ALIGN = 5,        /* a pointer is not 16-byte aligned             */
     ATTN_ERR_SCALE = 6,        /* scale is not finite or not > 0               */
     ATTN_ERR_HIP = 7,          /* the HIP runtime reported an error at launch  */
@@ -55,7 +55,8 @@ enum attn_fwd_status {
  *            Written completely: natural-log log-sum-exp of each row's
  *            scaled scores.  Required (not optional).
  *   B, H, N  batch, heads, sequence length (queries = keys = N).  Any of them
- *            may be 0 (nothing is launched).  N must be a multiple of 128.
+ *            may be 0 (nothing is launched); N need not be a multiple of any
+ *            tile size.  B*H*ceil(N/256) and N*d*2 must fit in an int.
  *   d        head dimension: 64 or 128.
  *   causal   0: every query sees every key.  Non-zero: query i sees keys
  *            0..i (lower-triangular mask, top-left aligned).

@@ -70,8 +70,6 @@ def call(B=2, H=3, N=256, d=128, causal=0, scale=0.088, q=FAKE, k=FAKE, v=FAKE, 
     (dict(scale=-0.1), af.Status.ERR_SCALE),
     (dict(scale=float("nan")), af.Status.ERR_SCALE),
     (dict(scale=float("inf")), af.Status.ERR_SCALE),
-    (dict(N=100), af.Status.ERR_SEQ_MULTIPLE),
-    (dict(N=4097), af.Status.ERR_SEQ_MULTIPLE),
     (dict(q=0), af.Status.ERR_NULL),
     (dict(k=0), af.Status.ERR_NULL),
     (dict(v=0), af.Status.ERR_NULL),
@@ -83,6 +81,7 @@ def call(B=2, H=3, N=256, d=128, causal=0, scale=0.088, q=FAKE, k=FAKE, v=FAKE, 
     (dict(o=FAKE + 1), af.Status.ERR_ALIGN),
     (dict(lse=FAKE + 4), af.Status.ERR_ALIGN),
     (dict(B=1 << 20, H=1 << 12, N=1 << 14), af.Status.ERR_SHAPE),
+    (dict(B=1 << 16, H=1 << 8, N=1 << 16, d=64), af.Status.ERR_SHAPE),
     (dict(B=1, H=1, N=1 << 24, d=128), af.Status.ERR_SHAPE),
     (dict(B=1, H=1, N=1 << 23, d=128), af.Status.ERR_SHAPE),
     (dict(B=1, H=1, N=1 << 24, d=64), af.Status.ERR_SHAPE),

@@ -28,6 +28,21 @@ SMALL = [
     (3, 1, 1152, 128, False, 2.0),
 ]
 
+# Sequence lengths that are not multiples of any tile: partial query tiles and
+# a partial last key block (keys >= N masked, queries >= N never stored).
+RAGGED = [
+    (1, 1, 1, 64, False),
+    (1, 2, 1, 128, True),
+    (2, 1, 31, 128, False),
+    (2, 1, 33, 64, True),
+    (1, 3, 100, 128, False),
+    (1, 3, 100, 64, True),
+    (2, 2, 257, 64, False),
+    (2, 2, 257, 128, True),
+    (1, 2, 1000, 128, True),
+    (1, 2, 1000, 64, False),
+]
+
 
 @pytest.mark.parametrize("B,H,N,d,causal,sigma", SMALL)
 def test_small_full(B, H, N, d, causal, sigma):
@@ -37,6 +52,16 @@ def test_small_full(B, H, N, d, causal, sigma):
     o, lse = run_gpu(q, k, v, causal, scale)
     o_ref, lse_ref = oracle.attention(q, k, v, causal, scale, threads=ORACLE_THREADS)
     assert_parity(to_host_f64(o), to_host_f64(lse), o_ref, lse_ref, "small")
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", RAGGED)
+def test_ragged_full(B, H, N, d, causal):
+    log(f"[ragged] B={B} H={H} N={N} d={d} causal={causal}")
+    q, k, v = make_qkv(B, H, N, d, seed=200 + N + d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run_gpu(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.attention(q, k, v, causal, scale, threads=ORACLE_THREADS)
+    assert_parity(to_host_f64(o), to_host_f64(lse), o_ref, lse_ref, "ragged")
 
 
 @pytest.mark.parametrize("name", ["B1-H1-N256-d64", "B16-H16-N1024-d64"])
