@@ -61,10 +61,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
-constexpr int kThreads = kWave * kWaves;
 constexpr int kQueriesPerWave = 32;
-constexpr int kBlockM = kWaves * kQueriesPerWave;  // queries per workgroup
+// Waves per workgroup: d=128 runs one 8-wave workgroup per CU (two waves per
+// SIMD; each K/V tile is fetched into LDS once per 256 queries); d=64 runs
+// 4-wave workgroups, three per CU (its register need allows three waves per
+// SIMD).
+template <int D>
+struct Launch {
+  static constexpr int kWaves = D == 128 ? 8 : 4;
+  static constexpr int kThreads = kWave * kWaves;
+  static constexpr int kBlockM = kWaves * kQueriesPerWave;  // queries per workgroup
+  static constexpr int kMinBlocks = D == 128 ? 1 : 2;      // launch-bounds occupancy hint
+};
 constexpr int kBlockN = 64;                        // keys per LDS stage
 constexpr int kXcds = 8;
 // O is rescaled only when a query's block maximum exceeds the reference
@@ -199,7 +207,7 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2)  // two waves per SIMD: <= 256 registers each
+__global__ __launch_bounds__(Launch<D>::kThreads, Launch<D>::kMinBlocks)  // <= 256 registers
 void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, __bf16* __restrict__ o,
                      float* __restrict__ lse, int N, float c) {
@@ -210,6 +218,8 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   constexpr int kDBlocks = T::kDBlocks;
   constexpr int kStageBytes = T::kStageBytes;
   constexpr int kRowsPerLoad = kWave * 16 / kRowBytes;              // rows one wave load fills
+  constexpr int kWaves = Launch<D>::kWaves;
+  constexpr int kBlockM = Launch<D>::kBlockM;
   constexpr int kLoadsPerWave = kBlockN / (kRowsPerLoad * kWaves);  // per tensor per stage
 
   // K stages 0,1 then V stages 0,1.
@@ -465,9 +475,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 template <int D, bool CAUSAL>
 int launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
            float c, hipStream_t stream) {
-  const int n_qt = (N + kBlockM - 1) / kBlockM;
+  const int n_qt = (N + Launch<D>::kBlockM - 1) / Launch<D>::kBlockM;
   const int grid = n_qt * BH;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL>), dim3(grid), dim3(Launch<D>::kThreads), 0, stream,
                      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, N, c);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -482,7 +492,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   if (!(scale > 0.0f) || !isfinite(scale)) return ATTN_ERR_SCALE;
   const int64_t bh = (int64_t)B * H;
   if (bh > INT32_MAX) return ATTN_ERR_SHAPE;
-  if (bh * (((int64_t)N + kBlockM - 1) / kBlockM) > INT32_MAX) return ATTN_ERR_SHAPE;  // grid
+  if (bh * (((int64_t)N + 127) / 128) > INT32_MAX) return ATTN_ERR_SHAPE;  // grid (any d)
   if ((int64_t)N * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;  // one head's bytes fit an int
   if (bh == 0 || N == 0) return ATTN_OK;
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
