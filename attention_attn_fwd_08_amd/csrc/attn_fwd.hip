@@ -162,6 +162,21 @@ struct Tile {
   static constexpr int kStageBytes = kBlockN * kRowBytes;
 };
 
+// Scores S^T of one 32-key block (sb) of a K stage against this wave's 32
+// queries.
+template <int D>
+__device__ __forceinline__ void scores_block(const unsigned char* k_lds, int sb,
+                                             const int (&k_off)[Tile<D>::kSteps],
+                                             const bf16x8 (&qf)[Tile<D>::kSteps], f32x16& s) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+  for (int st = 0; st < Tile<D>::kSteps; ++st) {
+    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(k_lds + sb * 32 * Tile<D>::kRowBytes + k_off[st]);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s, 0, 0, 0);
+  }
+}
+
 // Scores S^T of the two 32-key blocks of a K stage against this wave's 32
 // queries.  Accumulator register r of lane L: key 8*(r/4) + 4*(L/32) + r%4 of
 // the block, query L%32.
@@ -346,21 +361,46 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // One tile: s_cur holds tile t's (masked) scores, s_next receives tile
   // t+1's.  HAS_NEXT and MASK_NEXT are compile-time so the body is straight
   // line code the scheduler can interleave (MFMA of one phase against VALU).
+  // A 32-key block is live for this wave iff its first key is visible to at
+  // least one of the wave's queries; dead blocks (above the diagonal, or past
+  // N) skip their MFMAs and exponentials.  Only the steps that can meet one
+  // (masked successor, or the last tile) test this.
+  const int wave_last_key = CAUSAL ? min(q0 + kQueriesPerWave - 1, N - 1) : N - 1;
+  auto live = [&](int tile, int sb) __attribute__((always_inline)) {
+    return tile * kBlockN + sb * 32 <= wave_last_key;
+  };
   auto step = [&](auto has_next_tag, auto mask_next_tag, int t, f32x16(&s_cur)[2],
                   f32x16(&s_next)[2]) __attribute__((always_inline)) {
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
     constexpr bool MASK_NEXT = decltype(mask_next_tag)::value;
+    constexpr bool CHECK = MASK_NEXT || !HAS_NEXT;  // may meet dead blocks
     wait_lds_dma<0>();
     __syncthreads();  // K_{t+1} and V_t have landed; K_t and V_{t-1} are free
     if (t + 2 < n_tiles) load_k(t + 2, t & 1);
     if (HAS_NEXT) load_v(t + 1, (t + 1) & 1);
 
     // Phase A: probabilities of tile t (VALU) while S_{t+1} runs on MFMA.
-    if constexpr (HAS_NEXT) scores<D>(k_base + ((t + 1) & 1) * kStageBytes, k_off, qf, s_next);
+    if constexpr (HAS_NEXT) {
+      const unsigned char* const k_lds = k_base + ((t + 1) & 1) * kStageBytes;
+      if constexpr (CHECK) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          if (live(t + 1, sb)) {
+            scores_block<D>(k_lds, sb, k_off, qf, s_next[sb]);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s_next[sb][r] = -INFINITY;
+          }
+        }
+      } else {
+        scores<D>(k_lds, k_off, qf, s_next);
+      }
+    }
     const float mc = m_ref * c;
     bf16x8 pb[2][2];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < 2; ++sb) {
+      if (CHECK && !live(t, sb)) continue;  // its probabilities are all 0
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         float p[8];
@@ -371,11 +411,13 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         }
         l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       }
+    }
 
     // Phase B: O^T += V_t^T P_t^T on MFMA while the VALU reduces S_{t+1}.
     const unsigned char* const v_lds = v_base + (t & 1) * kStageBytes;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < 2; ++sb) {
+      if (CHECK && !live(t, sb)) continue;
 #pragma unroll
       for (int b = 0; b < kDBlocks; ++b)
 #pragma unroll
@@ -386,6 +428,7 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[sb][cc], acc[b], 0, 0, 0);
         }
+    }
     if constexpr (HAS_NEXT) {
       if constexpr (MASK_NEXT) mask_tile<CAUSAL>(s_next, (t + 1) * kBlockN, q0, N, l32, half);
       const float mx = tile_max(s_next);
