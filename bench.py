@@ -9,8 +9,12 @@ resident in HBM.  Prints ONE JSON line on stdout; progress goes to stderr.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 Throughput counts 4*B*H*N^2*d flops, halved for causal.  The kernel's own
-average duration comes from HIP events recorded around every launch on the
-stream the kernel runs on (torch's current stream, which the library is handed).
+duration comes from HIP events recorded around every launch on the stream the
+kernel runs on (torch's current stream, which the library is handed); the
+record gives its mean (the roofline figure), median, min and p90, the median of
+a second loop that overwrites a 512 MiB buffer between launches (L2 and MALL
+hold no input when each launch starts), and the shader clock that rocm-smi
+reports while the kernel runs back to back.
 The CPU baseline times the fp64 oracle on a bounded sample of query rows of
 the same workload on this host's cores, and reuses those oracle rows to check
 the benchmarked output.
@@ -60,6 +64,40 @@ def measured_traffic(workload: str):
     return entry.get("hbm_bytes_per_launch")
 
 
+def sample_sclk_mhz(run_for_s: float, launch) -> float | None:
+    """Median shader clock (MHz) that rocm-smi reports while `launch` runs back
+    to back for about `run_for_s` seconds; None when rocm-smi is unavailable."""
+    import subprocess
+    import threading
+    import torch
+    stop = threading.Event()
+
+    def busy():
+        while not stop.is_set():
+            for _ in range(8):
+                launch()
+            torch.cuda.synchronize()
+
+    th = threading.Thread(target=busy, daemon=True)
+    th.start()
+    samples = []
+    t_end = time.perf_counter() + run_for_s
+    try:
+        while time.perf_counter() < t_end:
+            out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                                 text=True, timeout=10).stdout
+            for card in json.loads(out).values():
+                for key, val in card.items():
+                    if "sclk" in key.lower() and "Mhz" in str(val):
+                        samples.append(float(str(val).strip("()Mhz")))
+    except (OSError, ValueError, subprocess.SubprocessError, AttributeError):
+        pass
+    finally:
+        stop.set()
+        th.join()
+    return float(sorted(samples)[len(samples) // 2]) if samples else None
+
+
 def cpu_baseline(w, q, k, v, target_gflop: float, threads: int):
     """Time the oracle on a bounded sample of rows; returns (record, rows, o, lse)."""
     import numpy as np
@@ -90,13 +128,15 @@ def cpu_baseline(w, q, k, v, target_gflop: float, threads: int):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-gflop", type=float, default=80.0,
                     help="size of the oracle sample for the CPU baseline (fp64 GFLOP)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle leg (for profiler runs)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the flushed-cache timing and the clock sample (for profiler runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB, 3 times (the "
                          "known-size reference that scales the HBM byte counters)")
@@ -166,8 +206,31 @@ def main() -> int:
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms_per_step = (t_end - t_begin) * 1e3 / args.steps
     kernel_ms = sum(launch_ms) / len(launch_ms)
-    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, kernel avg {kernel_ms:.4f} ms, "
-        f"min {min(launch_ms):.4f}, max {max(launch_ms):.4f}")
+    srt = sorted(launch_ms)
+    timing = {
+        "kernel_ms_mean": round(kernel_ms, 5),
+        "kernel_ms_median": round(srt[len(srt) // 2], 5),
+        "kernel_ms_min": round(srt[0], 5),
+        "kernel_ms_p90": round(srt[min(len(srt) - 1, int(0.9 * len(srt)))], 5),
+    }
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, kernel {timing}")
+
+    if not args.no_extras:
+        # Launches that start with nothing of the inputs in L2 or MALL.
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = []
+        for i in range(min(args.steps, 20)):
+            flush.fill_(i & 0xFF)
+            s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s_ev.record(stream)
+            step()
+            e_ev.record(stream)
+            torch.cuda.synchronize()
+            cold.append(s_ev.elapsed_time(e_ev))
+        del flush
+        timing["kernel_ms_median_flushed"] = round(sorted(cold)[len(cold) // 2], 5)
+        timing["sclk_mhz_rocm_smi"] = sample_sclk_mhz(2.0, step)
+        log(f"flushed median {timing['kernel_ms_median_flushed']} ms, sclk {timing['sclk_mhz_rocm_smi']}")
 
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     achieved = w.flops / (kernel_ms * 1e-3) / 1e12
@@ -200,10 +263,12 @@ def main() -> int:
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "kernel_avg_ms": round(kernel_ms, 5),
+            "kernel_tflops_at_median": round(w.flops / (timing["kernel_ms_median"] * 1e-3) / 1e12, 2),
             "flop_per_launch": w.flops,
             "algorithmic_hbm_bytes_per_launch": w.hbm_bytes,
         },
         "cpu_baseline": None,
+        "timing": timing,
     }
 
     ok = True

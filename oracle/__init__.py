@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.  Only ``tests/``,
 ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
 this package.  It shares no code with the HIP library and never imports it.
 
-The arithmetic lives in ``attn_oracle.c`` (single-threaded C, libm exp/log,
-fp64).  This module only compiles that file with gcc, loads it with ctypes and
+The arithmetic lives in ``attn_oracle.c`` (forward) and ``attn_bwd_oracle.c``
+(backward: the derivative of the same definition, full matrices per head), both
+single-threaded C with libm exp/log in fp64.  This module only compiles that file with gcc, loads it with ctypes and
 hands it buffers.  ``threads > 1`` splits the list of query rows between host
 threads, each running the same single-threaded C routine on its own rows (the
 rows are independent, so the result does not depend on the split).
@@ -32,21 +33,25 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "attn_oracle.c")
+SOURCES = (SOURCE, os.path.join(_HERE, "attn_bwd_oracle.c"))
 LIBRARY = os.path.join(_HERE, "libattn_oracle.so")
 
 _lock = threading.Lock()
 _lib = None
 
 
-def build(source: str = SOURCE, output: str = LIBRARY) -> str:
-    """Compile the oracle with gcc -O2 (no fast-math) into a shared library."""
+def build(sources=SOURCES, output: str = LIBRARY) -> str:
+    """Compile the oracle sources with gcc -O2 (no fast-math) into one shared
+    library.  ``sources`` may be one path or a sequence of paths."""
+    if isinstance(sources, str):
+        sources = (sources,)
     out_dir = os.path.dirname(os.path.abspath(output))
     fd, tmp = tempfile.mkstemp(suffix=".so.tmp", dir=out_dir)
     os.close(fd)
     try:
         subprocess.check_call(
             ["gcc", "-O2", "-std=c99", "-fno-fast-math", "-fPIC", "-shared",
-             "-o", tmp, source, "-lm"])
+             "-o", tmp, *sources, "-lm"])
         os.replace(tmp, output)
     finally:
         if os.path.exists(tmp):
@@ -60,6 +65,18 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
         u16p, u16p, u16p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double,
         ctypes.POINTER(ctypes.c_int64), i64, f64p, f64p]
     lib.attn_oracle_rows.restype = ctypes.c_int
+    if hasattr(lib, "attn_bwd_oracle_heads"):
+        lib.attn_bwd_oracle_heads.argtypes = [
+            u16p, u16p, u16p, u16p, i64, i64, i64, ctypes.c_int, ctypes.c_double, i64, i64,
+            f64p, f64p, f64p, f64p]
+        lib.attn_bwd_oracle_heads.restype = ctypes.c_int
+        lib.attn_fwd_oracle_head_f64.argtypes = [
+            f64p, f64p, f64p, i64, i64, ctypes.c_int, ctypes.c_double, f64p, f64p, f64p]
+        lib.attn_fwd_oracle_head_f64.restype = ctypes.c_int
+        lib.attn_bwd_oracle_head_f64.argtypes = [
+            f64p, f64p, f64p, f64p, i64, i64, ctypes.c_int, ctypes.c_double,
+            f64p, f64p, f64p, f64p, f64p, f64p, f64p]
+        lib.attn_bwd_oracle_head_f64.restype = ctypes.c_int
     return lib
 
 
@@ -72,7 +89,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     with _lock:
         if _lib is None:
             stale = (not os.path.exists(LIBRARY)
-                     or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE))
+                     or any(os.path.getmtime(LIBRARY) < os.path.getmtime(s) for s in SOURCES))
             if stale:
                 build()
             _lib = _declare(ctypes.CDLL(LIBRARY))
@@ -140,3 +157,80 @@ def attention(q, k, v, causal: bool, scale: float, threads: int = 1,
     B, H, N, d = q.shape
     o, lse = attention_rows(q, k, v, causal, scale, np.arange(B * H * N), threads, lib)
     return o.reshape(B, H, N, d), lse.reshape(B, H, N)
+
+
+# ---------------------------------------------------------------------------
+# Backward pass (the derivative of the forward definition; attn_bwd_oracle.c)
+# ---------------------------------------------------------------------------
+
+def attention_bwd(q, k, v, dout, causal: bool, scale: float, threads: int = 1,
+                  lib: ctypes.CDLL | None = None):
+    """Gradients of sum(O * dout) for bf16-bit inputs [B, H, N, d].
+
+    Returns ``(dq, dk, dv, delta)``: float64 [B,H,N,d] x 3 and [B,H,N], where
+    ``delta`` is the row sum of dout * O (O the exact forward output).
+    ``threads > 1`` splits the heads between host threads.
+    """
+    q, k, v = _check_inputs(q, k, v)
+    dout = np.ascontiguousarray(dout)
+    if dout.dtype != np.uint16 or dout.shape != q.shape:
+        raise TypeError("dout must be a uint16 array of bf16 bits shaped like q")
+    B, H, N, d = q.shape
+    BH = B * H
+    lib = lib or load()
+    dq = np.zeros((B, H, N, d)); dk = np.zeros_like(dq); dv = np.zeros_like(dq)
+    delta = np.zeros((B, H, N))
+    threads = max(1, min(int(threads), BH))
+    bounds = np.linspace(0, BH, threads + 1).astype(np.int64)
+
+    def run(part):
+        lo, hi = int(bounds[part]), int(bounds[part + 1])
+        if hi <= lo:
+            return 0
+        return lib.attn_bwd_oracle_heads(
+            _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
+            _ptr(dout, ctypes.c_uint16), BH, N, d, int(bool(causal)), float(scale), lo, hi,
+            _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double), _ptr(dv, ctypes.c_double),
+            _ptr(delta, ctypes.c_double))
+
+    if threads == 1:
+        statuses = [run(0)]
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as pool:
+            statuses = list(pool.map(run, range(threads)))
+    if any(s != 0 for s in statuses):
+        raise RuntimeError(f"oracle failed with status {statuses}")
+    return dq, dk, dv, delta
+
+
+def forward_head_f64(q, k, v, causal: bool, scale: float, lib: ctypes.CDLL | None = None):
+    """Forward of one head on float64 inputs [N, d]: returns (o, lse, p)."""
+    q, k, v = (np.ascontiguousarray(a, dtype=np.float64) for a in (q, k, v))
+    N, d = q.shape
+    lib = lib or load()
+    o = np.zeros((N, d)); lse = np.zeros(N); p = np.zeros((N, N))
+    st = lib.attn_fwd_oracle_head_f64(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
+                                      _ptr(v, ctypes.c_double), N, d, int(bool(causal)),
+                                      float(scale), _ptr(o, ctypes.c_double),
+                                      _ptr(lse, ctypes.c_double), _ptr(p, ctypes.c_double))
+    if st != 0:
+        raise RuntimeError(f"oracle failed with status {st}")
+    return o, lse, p
+
+
+def backward_head_f64(q, k, v, dout, causal: bool, scale: float,
+                      lib: ctypes.CDLL | None = None):
+    """Backward of one head on float64 inputs [N, d]: (dq, dk, dv, delta, o, lse)."""
+    q, k, v, dout = (np.ascontiguousarray(a, dtype=np.float64) for a in (q, k, v, dout))
+    N, d = q.shape
+    lib = lib or load()
+    dq = np.zeros((N, d)); dk = np.zeros((N, d)); dv = np.zeros((N, d))
+    delta = np.zeros(N); o = np.zeros((N, d)); lse = np.zeros(N)
+    scratch = np.zeros(2 * N * N)
+    f = lambda a: _ptr(a, ctypes.c_double)  # noqa: E731
+    st = lib.attn_bwd_oracle_head_f64(f(q), f(k), f(v), f(dout), N, d, int(bool(causal)),
+                                      float(scale), f(dq), f(dk), f(dv), f(delta), f(o), f(lse),
+                                      f(scratch))
+    if st != 0:
+        raise RuntimeError(f"oracle failed with status {st}")
+    return dq, dk, dv, delta, o, lse
