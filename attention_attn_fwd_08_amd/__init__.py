@@ -1,7 +1,7 @@
-"""MI355X-native fused attention forward: thin Python binding over the C ABI.
+"""MI355X-native fused attention: thin Python binding over the C ABI.
 
 Every step of the computation runs in the HIP library ``libattn_fwd.so``
-(built from ``csrc/attn_fwd.hip`` for gfx950).  This module only checks and
+(built from ``csrc/attn_fwd.hip`` and ``csrc/attn_bwd.hip`` for gfx950).  This module only checks and
 marshals arguments: PyTorch supplies device memory and the current stream.
 There is no fallback: if the library is missing, calls raise.
 
@@ -9,7 +9,12 @@ There is no fallback: if the library is missing, calls raise.
 
 computes o = softmax(scale * q k^T) v and lse = ln sum exp(scale * q k^T) per
 row, for bf16 tensors of shape [B, H, N, d] (the flash-attention forward of the
-ThunderKittens write-up, 88811315.cn, "H100 FlashAttention-2 forward example").
+ThunderKittens write-up, 88811315.cn, "H100 FlashAttention-2 forward example"), and
+
+    dq, dk, dv, delta = attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None)
+
+its derivative for a loss whose gradient with respect to o is ``dout``
+(``delta`` = rowsum(dout * o), the backward's per-row intermediate).
 """
 from __future__ import annotations
 
@@ -18,8 +23,8 @@ import math
 import os
 import threading
 
-__all__ = ["attn_fwd", "attn_fwd_raw", "attn_fwd_strerror", "load_library", "LIBRARY",
-           "Status", "AttnError"]
+__all__ = ["attn_fwd", "attn_fwd_raw", "attn_bwd", "attn_bwd_raw", "attn_fwd_strerror",
+           "load_library", "LIBRARY", "Status", "AttnError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_HERE, "libattn_fwd.so")
@@ -73,6 +78,8 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.attn_fwd_strerror.restype = ctypes.c_char_p
     lib.attn_fwd_abi_version.argtypes = []
     lib.attn_fwd_abi_version.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [vp] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float, vp]
+    lib.attn_bwd.restype = ctypes.c_int
     return lib
 
 
@@ -88,6 +95,75 @@ def attn_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
     return lib.attn_fwd(q_ptr or None, k_ptr or None, v_ptr or None, o_ptr or None,
                         lse_ptr or None, int(B), int(H), int(N), int(d), int(bool(causal)),
                         float(scale), stream or None)
+
+
+def attn_bwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, do_ptr: int,
+                 dq_ptr: int, dk_ptr: int, dv_ptr: int, delta_ptr: int,
+                 B: int, H: int, N: int, d: int, causal: bool, scale: float,
+                 stream: int = 0) -> int:
+    """Call the backward C entry point with raw integer addresses; returns the status."""
+    lib = load_library()
+    ptrs = [p or None for p in (q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr,
+                                dv_ptr, delta_ptr)]
+    return lib.attn_bwd(*ptrs, int(B), int(H), int(N), int(d), int(bool(causal)), float(scale),
+                        stream or None)
+
+
+def _check_bf16(name, t, shape, device):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.device.type != "cuda" or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be on the GPU device of q")
+    if t.dim() != 4 or not t.is_contiguous() or (shape is not None and t.shape != shape):
+        raise ValueError(f"{name} must be a contiguous tensor [B, H, N, d] shaped like q")
+
+
+def _check_f32(name, t, shape, device):
+    import torch
+    if (not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device != device
+            or tuple(t.shape) != shape or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous float32 tensor {list(shape)} on q's device")
+
+
+def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+             dq=None, dk=None, dv=None, delta=None):
+    """Attention backward on torch device tensors.
+
+    ``q, k, v, o, dout``: bf16 [B, H, N, d]; ``lse``: float32 [B, H, N] from
+    :func:`attn_fwd` with the same ``causal`` and ``scale``.  Returns
+    ``(dq, dk, dv, delta)`` (bf16 x3, float32 [B, H, N]); any of them may be
+    given to write into existing tensors.  Runs asynchronously on the current
+    stream of ``q``'s device.
+    """
+    import torch
+
+    _check_bf16("q", q, None, None)
+    shape, dev = q.shape, q.device
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_bf16(name, t, shape, dev)
+    B, H, N, d = shape
+    _check_f32("lse", lse, (B, H, N), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_bf16(name, t, shape, dev)
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    _check_f32("delta", delta, (B, H, N), dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        status = attn_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), delta.data_ptr(), B, H, N, d, causal, scale, stream)
+    if status != Status.OK:
+        raise AttnError(status, attn_fwd_strerror(status))
+    return dq, dk, dv, delta
 
 
 def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):

@@ -8,6 +8,7 @@ import tempfile
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCE = os.path.join(PKG, "csrc", "attn_fwd.hip")
+SOURCES = (SOURCE, os.path.join(PKG, "csrc", "attn_bwd.hip"))
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libattn_fwd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -24,7 +25,7 @@ def build(verbose: bool = False) -> str:
     """Build libattn_fwd.so in the package directory; returns its path."""
     fd, tmp = tempfile.mkstemp(suffix=".so.tmp", dir=PKG)
     os.close(fd)
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-o", tmp, SOURCE]
+    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-o", tmp, *SOURCES]
     try:
         res = subprocess.run(cmd, capture_output=True, text=True)
         noise = "is not a recognized feature for this target"

@@ -1,0 +1,557 @@
+// attn_bwd.hip -- attention backward for gfx950 (MI355X, CDNA4).
+//
+// The derivative of O = softmax(scale * Q K^T) V (ThunderKittens write-ups,
+// flash-attention forward examples; the backward is named there, not
+// listed), computed the flash-attention way: the N x N matrices are never
+// stored; P is recomputed tile by tile from Q, K and the forward's LSE.
+// Three kernels on one stream:
+//   1. delta_i = rowsum(dO_i * O_i)                     (memory bound)
+//   2. per 128-key block: dV^T += dO^T P and dK^T += Q^T dS while Q and dO
+//      stream through LDS (S = Q K^T, dP = dO V^T, dS = P o (dP - delta))
+//   3. per 128-query block: dQ^T += K^T dS^T while K and V stream through
+//      LDS (S^T = K Q^T, dP^T = V dO^T)
+// Mapping to CDNA4, as in the forward kernel: v_mfma_f32_32x32x16_bf16 with
+// the operand held for the whole workgroup (K and V in kernel 2, Q and dO in
+// kernel 3) in registers as the B operand, the streamed tile read from LDS as
+// the A operand, and the accumulator of one product reused in registers as
+// the B operand of the next (its 32-element column order is permuted the
+// same way in the transposed LDS reads, which the contraction does not see).
+// Tiles read both row-wise (ds_read_b128) and transposed
+// (ds_read_b64_tr_b16) use one XOR swizzle that is conflict-free for both.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <mutex>
+#include <stdint.h>
+#include <string.h>
+
+#include "attn_bwd.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kWave = 64;
+constexpr int kRows = 32;    // keys (kernel 2) or queries (kernel 3) per wave
+constexpr int kWaves = 4;    // waves per workgroup, one per SIMD
+constexpr int kBlock = kWaves * kRows;  // keys or queries per workgroup
+constexpr int kTile = 64;    // rows of a streamed LDS tile
+constexpr int kXcds = 8;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+template <int D>
+struct Geo {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kSteps = D / 16;    // MFMA k-steps over the head dimension
+  static constexpr int kDBlocks = D / 32;  // 32-row blocks of a transposed accumulator
+  static constexpr int kTileBytes = kTile * kRowBytes;
+  static constexpr int kRowsPerLoad = kWave * 16 / kRowBytes;        // rows one wave copy fills
+  static constexpr int kLoads = kTile / (kRowsPerLoad * kWaves);     // copies per wave per tile
+};
+
+// Chunk swizzle for a tile read both ways.  A row read (16 lanes read one
+// 16-byte chunk of 16 consecutive rows) needs the 16 rows in 16 distinct
+// bank groups; a transposed read (32 lanes read 4 rows x 4 adjacent chunks)
+// needs those 16 (row, chunk) pairs distinct.  d=128 (256-byte rows):
+// 4*(row%4) + 2*(row/4 %2) + (row/8 %2).  d=64 (128-byte rows, two per bank
+// sweep): 4*(row/2 %2) + (row/4 %4).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128) return 4 * (row & 3) + 2 * ((row >> 2) & 1) + ((row >> 3) & 1);
+  else return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+}
+
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  // Word 3 = 0x00020000: raw (untyped) 32-bit data for gfx9-family buffers.
+  return i32x4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes, 0x00020000};
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes global -> LDS (lane i writes LDS bytes [16i, 16i+16) after the
+// wave-uniform address in M0); offsets past the buffer size read as zeros.
+__device__ __forceinline__ void load16_to_lds(i32x4 rsrc, int voff, unsigned lds_addr) {
+  // The descriptor and the LDS address are wave-uniform: keep them in SGPRs.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ void wait_lds_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)(__attribute__((address_space(3))) const unsigned char*)p;
+}
+
+// Copy rows [row0, row0 + kTile) of a [N, D] bf16 matrix into a swizzled LDS
+// tile (rows past N read as zeros).  Every wave copies kLoads slices.
+template <int D>
+__device__ __forceinline__ void copy_tile(const __bf16* mat, int N, int row0, unsigned tile_lds,
+                                          int wave, int lane) {
+  using G = Geo<D>;
+  constexpr int kChunks = D / 8;
+  const i32x4 rsrc = make_rsrc(mat + (size_t)row0 * D, (N - row0) * G::kRowBytes);
+#pragma unroll
+  for (int it = 0; it < G::kLoads; ++it) {
+    const int r = (wave * G::kLoads + it) * G::kRowsPerLoad + lane / kChunks;
+    const int voff = r * G::kRowBytes + (((lane % kChunks) ^ swz<D>(r)) << 4);
+    load16_to_lds(rsrc, voff, tile_lds + (wave * G::kLoads + it) * G::kRowsPerLoad * G::kRowBytes);
+  }
+}
+
+// Copy kTile floats [row0, row0 + kTile) of a length-N vector into LDS (lanes
+// 0..15 of one wave; entries past N read as zeros).
+__device__ __forceinline__ void copy_vec(const float* vec, int N, int row0, unsigned dst, int lane) {
+  if (lane < kTile / 4) {
+    const i32x4 rsrc = make_rsrc(vec + row0, (N - row0) * 4);
+    load16_to_lds(rsrc, lane * 16, dst);
+  }
+}
+
+// Per-lane LDS byte offsets (tile-relative, for tile rows 0..31 of a 32-row
+// block) of the two operand reads.  Row read (A operand of X Y^T with X the
+// tile): row L%32, logical chunk 2*st + L/32.
+template <int D>
+__device__ __forceinline__ int row_off(int l32, int half, int st) {
+  return l32 * Geo<D>::kRowBytes + (((2 * st + half) ^ swz<D>(l32)) << 4);
+}
+// Transposed read (A operand of X^T Y): 16-lane group G = L/16 and s = L%16
+// read row 16*cc + 4*(G/2) + s/4 (+8 for the second read) and columns
+// 32*b + 16*(G%2) + 4*(s%4)..+3; lane L then holds column 32*b + L%32 of rows
+// 16cc + 4*(L/32) + 0..3 and 16cc + 8 + 4*(L/32) + 0..3 -- the row order of a
+// 32x32 accumulator's registers 8cc..8cc+7.
+template <int D>
+__device__ __forceinline__ int tr_off(int lane, int h, int b, int cc) {
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int r = 16 * cc + 4 * (g16 >> 1) + (s16 >> 2) + 8 * h;
+  const int col = 32 * b + 16 * (g16 & 1) + 4 * (s16 & 3);
+  return r * Geo<D>::kRowBytes + (((col >> 3) ^ swz<D>(r)) << 4) + (col & 7) * 2;
+}
+__device__ __forceinline__ bf16x8 read_tr(const unsigned char* base, int off_lo, int off_hi) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off_lo));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off_hi));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Logical workgroup id: workgroups are dispatched round-robin over the XCDs;
+// the remap gives each XCD a contiguous range, so the blocks of one head run
+// on one XCD and share its L2.
+__device__ __forceinline__ int logical_block() {
+  const int grid = gridDim.x;
+  int lid = blockIdx.x;
+  if (grid % kXcds == 0) lid = (lid % kXcds) * (grid / kXcds) + lid / kXcds;
+  return lid;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 1: delta_i = sum_t dO[i,t] * O[i,t].  Eight lanes per row.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const __bf16* __restrict__ o,
+                                                        const __bf16* __restrict__ dout,
+                                                        float* __restrict__ delta, long long rows) {
+  constexpr int kPer = D / 8;  // elements per lane: 16 (d=128) or 8 (d=64)
+  const long long row = (long long)blockIdx.x * 32 + threadIdx.x / 8;
+  const int sub = threadIdx.x & 7;
+  float acc = 0.f;
+  if (row < rows) {
+    const bf16x8* po = reinterpret_cast<const bf16x8*>(o + row * D + sub * kPer);
+    const bf16x8* pg = reinterpret_cast<const bf16x8*>(dout + row * D + sub * kPer);
+#pragma unroll
+    for (int c = 0; c < kPer / 8; ++c) {
+      const bf16x8 a = po[c], g = pg[c];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc = fmaf((float)a[j], (float)g[j], acc);
+    }
+  }
+  acc += __shfl_xor(acc, 1, 8);
+  acc += __shfl_xor(acc, 2, 8);
+  acc += __shfl_xor(acc, 4, 8);
+  if (sub == 0 && row < rows) delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2: dK, dV for one 128-key block of one head (32 keys per wave).
+// ---------------------------------------------------------------------------
+template <int D>
+struct KvLaunch {
+  static constexpr int kMinBlocks = D == 128 ? 1 : 2;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kWaves * kWave, KvLaunch<D>::kMinBlocks)
+void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                     const __bf16* __restrict__ v, const float* __restrict__ lse,
+                     const __bf16* __restrict__ dout, const float* __restrict__ delta,
+                     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int N, float scale, float c) {
+  using G = Geo<D>;
+  constexpr int kSteps = G::kSteps;
+  constexpr int kDBlocks = G::kDBlocks;
+  constexpr int kTileBytes = G::kTileBytes;
+  constexpr int kStageBytes = 2 * kTileBytes + 2 * kTile * 4;  // Q, dO, lse, delta
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+
+  const int n_kb = (N + kBlock - 1) / kBlock;
+  const int lid = logical_block();
+  const int head = lid / n_kb;
+  const int kb = lid % n_kb;
+  const size_t head_off = (size_t)head * N * D;
+  const __bf16* const qh = q + head_off;
+  const __bf16* const doh = dout + head_off;
+  const float* const lseh = lse + (size_t)head * N;
+  const float* const dlth = delta + (size_t)head * N;
+  const int key0 = kb * kBlock + wave * kRows;  // this wave's first key
+
+  // K^T and V^T as B operands: lane L holds key key0 + L%32 (rows past N: any
+  // valid row; their outputs are not stored), features 16*st + 8*(L/32)..+7.
+  bf16x8 kf[kSteps], vf[kSteps];
+  {
+    const int row = min(key0 + l32, N - 1);
+    const __bf16* kr = k + head_off + (size_t)row * D + 8 * half;
+    const __bf16* vr = v + head_off + (size_t)row * D + 8 * half;
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      kf[st] = *reinterpret_cast<const bf16x8*>(kr + 16 * st);
+      vf[st] = *reinterpret_cast<const bf16x8*>(vr + 16 * st);
+    }
+  }
+  f32x16 dkt[kDBlocks], dvt[kDBlocks];  // dK^T, dV^T: [d, keys]; lane = key
+#pragma unroll
+  for (int b = 0; b < kDBlocks; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dkt[b][r] = dvt[b][r] = 0.f;
+
+  int ro[kSteps];
+#pragma unroll
+  for (int st = 0; st < kSteps; ++st) ro[st] = row_off<D>(l32, half, st);
+  int tro[2][kDBlocks][2];  // [cc][b][h]
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int b = 0; b < kDBlocks; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) tro[cc][b][h] = tr_off<D>(lane, h, b, cc);
+
+  // Query tiles that see at least one key of the block.
+  const int qt_first = CAUSAL ? (kb * kBlock) / kTile : 0;
+  const int n_qt = (N + kTile - 1) / kTile;
+  auto stage_ptr = [&](int s) __attribute__((always_inline)) { return smem + s * kStageBytes; };
+  auto issue = [&](int qt, int s) __attribute__((always_inline)) {
+    unsigned char* st_base = stage_ptr(s);
+    const int row0 = qt * kTile;
+    copy_tile<D>(qh, N, row0, lds_addr(st_base), wave, lane);
+    copy_tile<D>(doh, N, row0, lds_addr(st_base + kTileBytes), wave, lane);
+    if (wave == 0) {
+      copy_vec(lseh, N, row0, lds_addr(st_base + 2 * kTileBytes), lane);
+      copy_vec(dlth, N, row0, lds_addr(st_base + 2 * kTileBytes + kTile * 4), lane);
+    }
+  };
+  if (qt_first < n_qt) issue(qt_first, 0);
+
+  for (int qt = qt_first; qt < n_qt; ++qt) {
+    const int s = (qt - qt_first) & 1;
+    wait_lds_dma_all();
+    __syncthreads();  // tile qt has landed; the other stage is free
+    if (qt + 1 < n_qt) issue(qt + 1, s ^ 1);
+    const unsigned char* const qt_lds = stage_ptr(s);
+    const unsigned char* const dot_lds = qt_lds + kTileBytes;
+    const float* const lse_lds = reinterpret_cast<const float*>(qt_lds + 2 * kTileBytes);
+    const float* const dlt_lds = lse_lds + kTile;
+
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qrow0 = qt * kTile + qb * kRows;
+      if (CAUSAL && qrow0 + kRows - 1 < key0) continue;  // every query precedes every key
+      const unsigned char* const qa = qt_lds + qb * kRows * G::kRowBytes;
+      const unsigned char* const da = dot_lds + qb * kRows * G::kRowBytes;
+      // S = Q K^T and dP = dO V^T: [queries, keys]; lane = key, register r =
+      // query 8*(r/4) + 4*(L/32) + r%4 of the block.
+      f32x16 sacc, pacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        sacc = mfma(*reinterpret_cast<const bf16x8*>(qa + ro[st]), kf[st], sacc);
+        pacc = mfma(*reinterpret_cast<const bf16x8*>(da + ro[st]), vf[st], pacc);
+      }
+      // P = 2^(s*c - lse*log2 e), dS = P (dP - delta); masked entries are 0.
+      const bool partial = (CAUSAL && qrow0 < key0 + kRows - 1) || qrow0 + kRows > N;
+      bf16x8 pb[2], sb[2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qi = qb * kRows + 8 * g + 4 * half;  // tile row of registers 4g..4g+3
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_lds + qi);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt_lds + qi);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * g + j;
+          float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -l4[j] * kLog2e));
+          if (partial) {
+            const int query = qt * kTile + qi + j;
+            const bool vis = CAUSAL ? (key0 + l32 <= query && query < N) : (query < N);
+            p = vis ? p : 0.f;
+          }
+          const float ds = p * (pacc[r] - d4[j]);
+          pb[r >> 3][r & 7] = (__bf16)p;
+          sb[r >> 3][r & 7] = (__bf16)ds;
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-query steps.
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int b = 0; b < kDBlocks; ++b) {
+          dvt[b] = mfma(read_tr(da, tro[cc][b][0], tro[cc][b][1]), pb[cc], dvt[b]);
+          dkt[b] = mfma(read_tr(qa, tro[cc][b][0], tro[cc][b][1]), sb[cc], dkt[b]);
+        }
+    }
+  }
+
+  // Epilogue: lane = key; registers 4j..4j+3 of block b are features
+  // 32b + 8j + 4*(L/32) + 0..3.
+  const int key = key0 + l32;
+  if (key < N) {
+    __bf16* const kr = dk + head_off + (size_t)key * D;
+    __bf16* const vr = dv + head_off + (size_t)key * D;
+#pragma unroll
+    for (int b = 0; b < kDBlocks; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 kv4, vv4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          kv4[r] = (__bf16)(dkt[b][4 * j + r] * scale);
+          vv4[r] = (__bf16)dvt[b][4 * j + r];
+        }
+        *reinterpret_cast<bf16x4*>(kr + 32 * b + 8 * j + 4 * half) = kv4;
+        *reinterpret_cast<bf16x4*>(vr + 32 * b + 8 * j + 4 * half) = vv4;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 3: dQ for one 128-query block of one head (32 queries per wave).
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kWaves * kWave, 2)
+void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                   const __bf16* __restrict__ v, const float* __restrict__ lse,
+                   const __bf16* __restrict__ dout, const float* __restrict__ delta,
+                   __bf16* __restrict__ dq, int N, float scale, float c) {
+  using G = Geo<D>;
+  constexpr int kSteps = G::kSteps;
+  constexpr int kDBlocks = G::kDBlocks;
+  constexpr int kTileBytes = G::kTileBytes;
+  constexpr int kStageBytes = 2 * kTileBytes;  // K, V
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int l32 = lane & 31;
+  const int half = lane >> 5;
+
+  const int n_qb = (N + kBlock - 1) / kBlock;
+  const int lid = logical_block();
+  const int head = lid / n_qb;
+  const int qb = CAUSAL ? n_qb - 1 - lid % n_qb : lid % n_qb;  // causal: longest first
+  const size_t head_off = (size_t)head * N * D;
+  const __bf16* const kh = k + head_off;
+  const __bf16* const vh = v + head_off;
+  const int q0 = qb * kBlock + wave * kRows;  // this wave's first query
+
+  // Q^T and dO^T as B operands: lane L holds query q0 + L%32 (rows past N: any
+  // valid row, not stored), features 16*st + 8*(L/32)..+7.
+  bf16x8 qf[kSteps], gf[kSteps];
+  const int row = min(q0 + l32, N - 1);
+  {
+    const __bf16* qr = q + head_off + (size_t)row * D + 8 * half;
+    const __bf16* gr = dout + head_off + (size_t)row * D + 8 * half;
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      qf[st] = *reinterpret_cast<const bf16x8*>(qr + 16 * st);
+      gf[st] = *reinterpret_cast<const bf16x8*>(gr + 16 * st);
+    }
+  }
+  const float lse2 = lse[(size_t)head * N + row] * kLog2e;
+  const float dlt = delta[(size_t)head * N + row];
+  const int query = q0 + l32;
+
+  f32x16 dqt[kDBlocks];  // dQ^T: [d, queries]; lane = query
+#pragma unroll
+  for (int b = 0; b < kDBlocks; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqt[b][r] = 0.f;
+
+  int ro[kSteps];
+#pragma unroll
+  for (int st = 0; st < kSteps; ++st) ro[st] = row_off<D>(l32, half, st);
+  int tro[2][kDBlocks][2];
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int b = 0; b < kDBlocks; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) tro[cc][b][h] = tr_off<D>(lane, h, b, cc);
+
+  const int kv_end = CAUSAL ? min((qb + 1) * kBlock, N) : N;
+  const int n_kt = (kv_end + kTile - 1) / kTile;
+  const int wave_last_key = CAUSAL ? min(q0 + kRows - 1, N - 1) : N - 1;
+  auto issue = [&](int kt, int s) __attribute__((always_inline)) {
+    unsigned char* st_base = smem + s * kStageBytes;
+    copy_tile<D>(kh, N, kt * kTile, lds_addr(st_base), wave, lane);
+    copy_tile<D>(vh, N, kt * kTile, lds_addr(st_base + kTileBytes), wave, lane);
+  };
+  if (n_kt > 0) issue(0, 0);
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int s = kt & 1;
+    wait_lds_dma_all();
+    __syncthreads();  // tile kt has landed; the other stage is free
+    if (kt + 1 < n_kt) issue(kt + 1, s ^ 1);
+    const unsigned char* const k_lds = smem + s * kStageBytes;
+    const unsigned char* const v_lds = k_lds + kTileBytes;
+    const bool partial = kt * kTile + kTile - 1 > wave_last_key || (CAUSAL && kt * kTile + kTile - 1 > q0);
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      const int key0 = kt * kTile + sb * kRows;
+      if (key0 > wave_last_key) continue;  // no query of this wave sees the block
+      const unsigned char* const ka = k_lds + sb * kRows * G::kRowBytes;
+      const unsigned char* const va = v_lds + sb * kRows * G::kRowBytes;
+      // S^T = K Q^T and dP^T = V dO^T: [keys, queries]; lane = query,
+      // register r = key 8*(r/4) + 4*(L/32) + r%4 of the block.
+      f32x16 sacc, pacc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        sacc = mfma(*reinterpret_cast<const bf16x8*>(ka + ro[st]), qf[st], sacc);
+        pacc = mfma(*reinterpret_cast<const bf16x8*>(va + ro[st]), gf[st], pacc);
+      }
+      bf16x8 sbf[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -lse2));
+        if (partial) {
+          const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool vis = key < N && (!CAUSAL || key <= query);
+          p = vis ? p : 0.f;
+        }
+        sbf[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - dlt));
+      }
+      // dQ^T += K^T dS^T over the block's two 16-key steps.
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int b = 0; b < kDBlocks; ++b)
+          dqt[b] = mfma(read_tr(ka, tro[cc][b][0], tro[cc][b][1]), sbf[cc], dqt[b]);
+    }
+  }
+
+  if (query < N) {
+    __bf16* const qr = dq + head_off + (size_t)query * D;
+#pragma unroll
+    for (int b = 0; b < kDBlocks; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 x;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = (__bf16)(dqt[b][4 * j + r] * scale);
+        *reinterpret_cast<bf16x4*>(qr + 32 * b + 8 * j + 4 * half) = x;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::once_flag g_once[kMaxDevices];
+bool g_gfx950[kMaxDevices];
+
+bool device_is_gfx950(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return false;
+  std::call_once(g_once[dev], [dev] {
+    hipDeviceProp_t prop;
+    g_gfx950[dev] = hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+                    strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  });
+  return g_gfx950[dev];
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <int D, bool CAUSAL>
+int launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, float* delta, int BH, int N, float scale,
+           hipStream_t stream) {
+  const long long rows = (long long)BH * N;
+  const float c = scale * kLog2e;
+  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream,
+                     static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), delta, rows);
+  const int n_blk = (N + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_blk * BH), dim3(kWaves * kWave), 0, stream,
+                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                     static_cast<const __bf16*>(v), lse, static_cast<const __bf16*>(dout), delta,
+                     static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), N, scale, c);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_blk * BH), dim3(kWaves * kWave), 0, stream,
+                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                     static_cast<const __bf16*>(v), lse, static_cast<const __bf16*>(dout), delta,
+                     static_cast<__bf16*>(dq), N, scale, c);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        float* delta, int B, int H, int N, int d, int causal, float scale,
+                        void* stream) {
+  if (B < 0 || H < 0 || N < 0) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (!(scale > 0.0f) || !isfinite(scale)) return ATTN_ERR_SCALE;
+  const int64_t bh = (int64_t)B * H;
+  if (bh > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (bh * (((int64_t)N + kBlock - 1) / kBlock) > INT32_MAX) return ATTN_ERR_SHAPE;  // grid
+  if ((int64_t)N * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;  // one head's bytes fit an int
+  if (bh * N > (int64_t)INT32_MAX * 32) return ATTN_ERR_SHAPE;  // delta grid
+  if (bh == 0 || N == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, delta};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_ALIGN;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+  if (!device_is_gfx950(dev)) return ATTN_ERR_DEVICE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int BH = static_cast<int>(bh);
+  if (d == 64) {
+    return causal ? launch<64, true>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, scale, s)
+                  : launch<64, false>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, scale, s);
+  }
+  return causal ? launch<128, true>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, scale, s)
+                : launch<128, false>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, scale, s);
+}

@@ -5,9 +5,10 @@ numpy's PCG64 generator, rounds them to bf16 on their bit patterns, and names
 the workloads.  Both the HIP path (through its tests and benchmark) and the
 oracle receive the very same bf16 bytes from here.
 
-Recipe: ``rng = numpy.random.default_rng(seed)``; Q, then K, then V are drawn,
-each as ``rng.standard_normal(B*H*N*d, dtype=float32) * sigma`` and rounded to
-bf16 with round-to-nearest-even.  Layout [B, H, N, d], contiguous row-major.
+Recipe: ``rng = numpy.random.default_rng(seed)``; Q, then K, then V (then, for
+the backward, dO) are drawn, each as
+``rng.standard_normal(B*H*N*d, dtype=float32) * sigma`` and rounded to bf16
+with round-to-nearest-even.  Layout [B, H, N, d], contiguous row-major.
 """
 from __future__ import annotations
 
@@ -97,6 +98,21 @@ def make_qkv(B: int, H: int, N: int, d: int, seed: int,
     n = B * H * N * d
     out = []
     for sigma in (qk_sigma, qk_sigma, v_sigma):
+        x = rng.standard_normal(n, dtype=np.float32)
+        if sigma != 1.0:
+            x = x * np.float32(sigma)
+        out.append(f32_to_bf16_bits(x).reshape(B, H, N, d))
+    return tuple(out)
+
+
+def make_qkv_dout(B: int, H: int, N: int, d: int, seed: int,
+                  qk_sigma: float = 1.0, v_sigma: float = 1.0, dout_sigma: float = 1.0):
+    """Seeded bf16 Q, K, V (the same arrays as ``make_qkv``) and then dO, the
+    next draw of the same generator: four uint16 bit arrays [B, H, N, d]."""
+    rng = np.random.default_rng(seed)
+    n = B * H * N * d
+    out = []
+    for sigma in (qk_sigma, qk_sigma, v_sigma, dout_sigma):
         x = rng.standard_normal(n, dtype=np.float32)
         if sigma != 1.0:
             x = x * np.float32(sigma)

@@ -6,7 +6,12 @@ tile schedule, Q load, K/V streaming, both MFMA products, online softmax and
 the O/LSE epilogue) over one batch of seeded synthetic inputs that are already
 resident in HBM.  Prints ONE JSON line on stdout; progress goes to stderr.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
+
+With ``--pass bwd`` a step is one call of the backward (delta, dK/dV and dQ
+kernels) on the same workload, with dO the next draw of the input generator;
+it counts 10*B*H*N^2*d flops (the five products QK^T, dO V^T, P^T dO, dS^T Q,
+dS K), halved for causal.
 
 Throughput counts 4*B*H*N^2*d flops, halved for causal.  The kernel's own
 duration comes from HIP events recorded around every launch on the stream the
@@ -31,7 +36,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from attention_attn_fwd_08_amd.inputs import HEADLINE, WORKLOADS, sample_rows, workload_inputs  # noqa: E402
+from attention_attn_fwd_08_amd.inputs import (HEADLINE, WORKLOADS, make_qkv_dout, sample_rows,  # noqa: E402
+                                              workload_inputs)
 
 # MI355X published dense bf16 MFMA peak: 256 CUs x 4096 flop/clk/CU x 2.4 GHz.
 PEAK_BF16_TFLOPS = 2516.6
@@ -125,12 +131,31 @@ def cpu_baseline(w, q, k, v, target_gflop: float, threads: int):
     return rec, rows, o_ref, lse_ref
 
 
+def cpu_baseline_bwd(w, q, k, v, dout, threads: int):
+    """Time the backward oracle on one head (the first); returns (record, grads)."""
+    import numpy as np
+    import oracle
+    sub = [np.ascontiguousarray(x[:1, :1]) for x in (q, k, v, dout)]
+    oracle.load()
+    t0 = time.perf_counter()
+    grads = oracle.attention_bwd(*sub, w.causal, w.scale, threads=1)
+    dt = time.perf_counter() - t0
+    flop = 10.0 * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+    rec = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+           "sample": (f"backward of head (0,0) of {w.name} ({flop / 1e9:.1f} GFLOP by the "
+                      f"10*N^2*d count; the oracle forms full N x N matrices) in {dt:.2f} s "
+                      f"on 1 thread")}
+    return rec, grads
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
+                    help="time the forward (default) or the backward")
     ap.add_argument("--cpu-gflop", type=float, default=80.0,
                     help="size of the oracle sample for the CPU baseline (fp64 GFLOP)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -173,7 +198,11 @@ def main() -> int:
     log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
 
     t0 = time.perf_counter()
-    q_bits, k_bits, v_bits = workload_inputs(w)
+    if args.which == "bwd":
+        q_bits, k_bits, v_bits, g_bits = make_qkv_dout(w.B, w.H, w.N, w.d, w.seed, w.qk_sigma,
+                                                       w.v_sigma)
+    else:
+        q_bits, k_bits, v_bits = workload_inputs(w)
     log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
 
     def dev_tensor(bits):
@@ -184,8 +213,20 @@ def main() -> int:
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
-    def step():
+    flops = w.flops
+    if args.which == "bwd":
+        g = dev_tensor(g_bits)
         af.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        delta = torch.empty_like(lse)
+        flops = 2.5 * w.flops
+
+        def step():
+            af.attn_bwd(q, k, v, o, lse, g, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv,
+                        delta=delta)
+    else:
+        def step():
+            af.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -232,12 +273,13 @@ def main() -> int:
         timing["sclk_mhz_rocm_smi"] = sample_sclk_mhz(2.0, step)
         log(f"flushed median {timing['kernel_ms_median_flushed']} ms, sclk {timing['sclk_mhz_rocm_smi']}")
 
-    value = w.flops / (ms_per_step * 1e-3) / 1e12
-    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
-    traffic = measured_traffic(w.name)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    traffic = measured_traffic(w.name) if args.which == "fwd" else None
 
     result = {
-        "metric": "attention fwd TFLOP/s at 1 MI355X and % of bf16 MFMA peak",
+        "metric": ("attention fwd TFLOP/s at 1 MI355X and % of bf16 MFMA peak" if args.which == "fwd"
+                   else "attention bwd TFLOP/s at 1 MI355X (10*B*H*N^2*d flops, causal halved)"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -253,6 +295,7 @@ def main() -> int:
             "workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
             "causal": w.causal, "scale": w.scale, "seed": w.seed,
             "qk_sigma": w.qk_sigma, "v_sigma": w.v_sigma, "parallelism": "none",
+            "pass": args.which,
         },
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
@@ -263,8 +306,8 @@ def main() -> int:
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "kernel_avg_ms": round(kernel_ms, 5),
-            "kernel_tflops_at_median": round(w.flops / (timing["kernel_ms_median"] * 1e-3) / 1e12, 2),
-            "flop_per_launch": w.flops,
+            "kernel_tflops_at_median": round(flops / (timing["kernel_ms_median"] * 1e-3) / 1e12, 2),
+            "flop_per_launch": flops,
             "algorithmic_hbm_bytes_per_launch": w.hbm_bytes,
         },
         "cpu_baseline": None,
@@ -272,7 +315,24 @@ def main() -> int:
     }
 
     ok = True
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.which == "bwd" and w.N * w.N * w.d > (4096 * 4096 * 128):
+        log("backward oracle skipped: one head of this workload is beyond the bench's CPU budget")
+    elif not args.no_cpu_baseline and args.which == "bwd":
+        log("backward oracle on one head ...")
+        rec, ref = cpu_baseline_bwd(w, q_bits, k_bits, v_bits, g_bits, 1)
+        result["cpu_baseline"] = rec
+        result["roofline"]["unit_of_launch"] = "whole backward: delta, dK/dV and dQ kernels"
+        parity = {"heads": 1}
+        for name, t, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref[:3]):
+            a = t[:1, :1].float().cpu().numpy().astype(np.float64)
+            e = np.abs(a - r)
+            parity[f"{name}_max_rel"] = float(e.max() / max(np.abs(r).max(), 1e-30))
+            parity[f"{name}_mean_rel"] = float(e.mean() / max(np.abs(r).mean(), 1e-30))
+        ok = all(v <= 1e-2 for k_, v in parity.items() if k_.endswith("_rel"))
+        parity["ok"] = ok
+        result["parity"] = parity
+        log(f"oracle: {rec['sample']}; parity {parity}")
+    elif not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))
         log(f"oracle sample on {threads} host threads ...")
         rec, rows, o_ref, lse_ref = cpu_baseline(w, q_bits, k_bits, v_bits, args.cpu_gflop,

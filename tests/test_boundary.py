@@ -1,11 +1,12 @@
-"""The C ABI: the library loads, exports what include/attn_fwd.h declares, and
-rejects bad arguments before touching the GPU.
+"""The C ABI: the library loads, exports what include/*.h declare, and rejects
+bad arguments before touching the GPU.
 
 Every call here fails validation (or is empty) by construction, so no HIP call
 is made and the fake addresses are never dereferenced; these tests run on a
 machine without a GPU.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -15,6 +16,7 @@ import attention_attn_fwd_08_amd as af
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
 
@@ -28,13 +30,17 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"}
+    return sorted(names)
 
 
-def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_fwd_abi_version", "attn_fwd_strerror"]
+def test_headers_declare_the_entry_points():
+    assert [os.path.basename(h) for h in HEADERS] == ["attn_bwd.h", "attn_fwd.h"]
+    assert declared_functions() == ["attn_bwd", "attn_fwd", "attn_fwd_abi_version",
+                                    "attn_fwd_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -116,3 +122,39 @@ def test_no_undefined_kernel_stubs(lib):
     out = subprocess.run([nm, "-D", af.LIBRARY], capture_output=True, text=True).stdout
     undefined = [ln for ln in out.splitlines() if " U " in ln and "__device_stub__" in ln]
     assert not undefined, undefined
+
+
+def call_bwd(B=2, H=3, N=256, d=128, causal=0, scale=0.088, **ptrs):
+    names = ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta")
+    p = [ptrs.get(n, FAKE) for n in names]
+    return af.attn_bwd_raw(*p, B, H, N, d, causal, scale)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), af.Status.ERR_SHAPE),
+    (dict(N=-1), af.Status.ERR_SHAPE),
+    (dict(d=32), af.Status.ERR_HEAD_DIM),
+    (dict(d=256), af.Status.ERR_HEAD_DIM),
+    (dict(scale=0.0), af.Status.ERR_SCALE),
+    (dict(scale=float("nan")), af.Status.ERR_SCALE),
+    (dict(B=1, H=1, N=1 << 24, d=128), af.Status.ERR_SHAPE),
+    (dict(B=1 << 20, H=1 << 12, N=1 << 14), af.Status.ERR_SHAPE),
+] + [(dict(**{n: 0}), af.Status.ERR_NULL)
+     for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta")]
+  + [(dict(**{n: FAKE + 4}), af.Status.ERR_ALIGN)
+     for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta")])
+def test_bwd_rejects(lib, kw, status):
+    assert call_bwd(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=0, q=0, dq=0, delta=0)])
+def test_bwd_empty_problem_is_a_noop(lib, kw):
+    assert call_bwd(**kw) == af.Status.OK
+
+
+def test_python_bwd_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 64)
+    with pytest.raises(ValueError):
+        af.attn_bwd(x, x, x, x, lse, x)
