@@ -23,8 +23,8 @@ import math
 import os
 import threading
 
-__all__ = ["attn_fwd", "attn_fwd_raw", "attn_bwd", "attn_bwd_raw", "attn_fwd_strerror",
-           "load_library", "LIBRARY", "Status", "AttnError"]
+__all__ = ["attn_fwd", "attn_fwd_raw", "attn_fwd_ex", "attn_fwd_ex_raw", "attn_bwd",
+           "attn_bwd_raw", "attn_fwd_strerror", "load_library", "LIBRARY", "Status", "AttnError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_HERE, "libattn_fwd.so")
@@ -78,6 +78,8 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.attn_fwd_strerror.restype = ctypes.c_char_p
     lib.attn_fwd_abi_version.argtypes = []
     lib.attn_fwd_abi_version.restype = ctypes.c_int
+    lib.attn_fwd_ex.argtypes = [vp] * 5 + [ctypes.c_int] * 6 + [ctypes.c_float, vp]
+    lib.attn_fwd_ex.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [vp] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float, vp]
     lib.attn_bwd.restype = ctypes.c_int
     return lib
@@ -205,6 +207,48 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
         stream = torch.cuda.current_stream(q.device).cuda_stream
         status = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                               lse.data_ptr(), B, H, N, d, causal, scale, stream)
+    if status != Status.OK:
+        raise AttnError(status, attn_fwd_strerror(status))
+    return out, lse
+
+
+def attn_fwd_ex_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
+                    B: int, H: int, Nq: int, Nk: int, d: int, causal: bool, scale: float,
+                    stream: int = 0) -> int:
+    """Call attn_fwd_ex with raw integer addresses; returns the status."""
+    lib = load_library()
+    return lib.attn_fwd_ex(q_ptr or None, k_ptr or None, v_ptr or None, o_ptr or None,
+                           lse_ptr or None, int(B), int(H), int(Nq), int(Nk), int(d),
+                           int(bool(causal)), float(scale), stream or None)
+
+
+def attn_fwd_ex(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """Attention forward for q [B, H, Nq, d] against k, v [B, H, Nk, d].
+
+    Causal masks are aligned bottom-right (key j visible to query i iff
+    j <= i + Nk - Nq); rows that see no key come back as o = 0, lse = -inf.
+    Returns ``(o, lse)`` like :func:`attn_fwd`.
+    """
+    import torch
+
+    _check_bf16("q", q, None, None)
+    B, H, Nq, d = q.shape
+    _check_bf16("k", k, None, q.device)
+    if k.shape[:2] != (B, H) or k.shape[3] != d:
+        raise ValueError("k must be [B, H, Nk, d] with q's B, H and d")
+    _check_bf16("v", v, k.shape, q.device)
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    _check_bf16("out", out, q.shape, q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_f32("lse", lse, (B, H, Nq), q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        status = attn_fwd_ex_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr(), B, H, Nq, Nk, d, causal, scale, stream)
     if status != Status.OK:
         raise AttnError(status, attn_fwd_strerror(status))
     return out, lse

@@ -221,11 +221,17 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
   return pair_max(fmaxf(m0, m1));
 }
 
-template <int D, bool CAUSAL>
+// N is the number of queries.  GENERAL: the keys number Nk (not N) and a
+// causal mask is offset by `off` (key j visible to query i iff j <= i + off);
+// rows that see no key get o = 0 and lse = -inf.  Otherwise Nk = N, off = 0
+// and every row sees key 0.
+template <int D, bool CAUSAL, bool GENERAL>
 __global__ __launch_bounds__(Launch<D>::kThreads, Launch<D>::kMinBlocks)  // <= 256 registers
 void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, __bf16* __restrict__ o,
-                     float* __restrict__ lse, int N, float c) {
+                     float* __restrict__ lse, int N, float c, int nk_arg, int off_arg) {
+  const int Nk = GENERAL ? nk_arg : N;
+  const int off = GENERAL ? off_arg : 0;
   using T = Tile<D>;
   constexpr int kRowBytes = T::kRowBytes;
   constexpr int kChunksPerRow = D / 8;
@@ -261,18 +267,43 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int qt = CAUSAL ? n_qt - 1 - lid % n_qt : lid % n_qt;
 
   const size_t head_off = (size_t)head * N * D;
+  const size_t kv_head_off = (size_t)head * Nk * D;
   const __bf16* const qh = q + head_off;
-  const __bf16* const kh = k + head_off;
-  const __bf16* const vh = v + head_off;
+  const __bf16* const kh = k + kv_head_off;
+  const __bf16* const vh = v + kv_head_off;
   const int q0 = qt * kBlockM + wave * kQueriesPerWave;  // this wave's first query
 
   // Tiles this workgroup visits; tiles from first_mask on are masked:
   // causal, the tiles on the diagonal of at least one of its waves; else
   // only a last tile that runs past N.
-  const int kv_end = CAUSAL ? min((qt + 1) * kBlockM, N) : N;
+  const int kv_end = CAUSAL ? min((qt + 1) * kBlockM + off, Nk) : Nk;
   const int n_tiles = (kv_end + kBlockN - 1) / kBlockN;
-  const int first_mask = CAUSAL ? qt * (kBlockM / kBlockN)
-                                : (N % kBlockN ? n_tiles - 1 : n_tiles);
+  int first_mask;
+  if constexpr (!GENERAL) {
+    first_mask = CAUSAL ? qt * (kBlockM / kBlockN) : (N % kBlockN ? n_tiles - 1 : n_tiles);
+  } else if constexpr (CAUSAL) {
+    // Tiles wholly at or below the workgroup's first query (+ off) need no mask.
+    const int first_last_key = qt * kBlockM + off;  // last key its first query sees
+    first_mask = first_last_key < 0 ? 0 : min((first_last_key + 1) / kBlockN, n_tiles);
+    if (kv_end == Nk && Nk % kBlockN) first_mask = min(first_mask, n_tiles - 1);
+  } else {
+    first_mask = Nk % kBlockN ? n_tiles - 1 : n_tiles;
+  }
+  if constexpr (GENERAL) {
+    if (n_tiles <= 0) {  // no query of the workgroup sees a key
+      const int qrow = q0 + l32;
+      if (qrow < N) {
+        __bf16* const orow = o + head_off + (size_t)qrow * D;
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * j + 4 * half) = bf16x4{0, 0, 0, 0};
+        if (half == 0) lse[(size_t)head * N + qrow] = -INFINITY;
+      }
+      return;
+    }
+  }
 
   // Global -> LDS copy of one K or V tile.  Lane i of a wave load fills
   // bytes [16i, 16i+16) after the wave's base: row base+i/kChunksPerRow,
@@ -291,7 +322,7 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                             wave * kLoadsPerWave * kRowsPerLoad * kRowBytes;
   auto load_tile = [&](const __bf16* base, const int (&ld_off)[kLoadsPerWave], int region,
                        int tile, int stage) __attribute__((always_inline)) {
-    const i32x4 rsrc = make_rsrc(base + (size_t)tile * kBlockN * D, (N - tile * kBlockN) * kRowBytes);
+    const i32x4 rsrc = make_rsrc(base + (size_t)tile * kBlockN * D, (Nk - tile * kBlockN) * kRowBytes);
     const unsigned dst = lds_wave + (2 * region + stage) * kStageBytes;
 #pragma unroll
     for (int it = 0; it < kLoadsPerWave; ++it)
@@ -354,7 +385,7 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // holds key 0, which every query sees, so the maximum is finite.
   f32x16 s_a[2], s_b[2];
   scores<D>(k_base, k_off, qf, s_a);
-  if (first_mask == 0) mask_tile<CAUSAL>(s_a, 0, q0, N, l32, half);
+  if (first_mask == 0) mask_tile<CAUSAL>(s_a, 0, q0 + off, Nk, l32, half);
   float m_ref = tile_max(s_a);  // reference maximum (raw score units), query q0+L%32
   float l_run = 0.f;            // this lane's half of the normaliser
 
@@ -365,7 +396,7 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // least one of the wave's queries; dead blocks (above the diagonal, or past
   // N) skip their MFMAs and exponentials.  Only the steps that can meet one
   // (masked successor, or the last tile) test this.
-  const int wave_last_key = CAUSAL ? min(q0 + kQueriesPerWave - 1, N - 1) : N - 1;
+  const int wave_last_key = CAUSAL ? min(q0 + kQueriesPerWave - 1 + off, Nk - 1) : Nk - 1;
   auto live = [&](int tile, int sb) __attribute__((always_inline)) {
     return tile * kBlockN + sb * 32 <= wave_last_key;
   };
@@ -396,7 +427,8 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         scores<D>(k_lds, k_off, qf, s_next);
       }
     }
-    const float mc = m_ref * c;
+    // A row that has seen no key yet has m_ref = -inf and only -inf scores.
+    const float mc = (GENERAL && m_ref == -INFINITY) ? 0.f : m_ref * c;
     bf16x8 pb[2][2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
@@ -430,7 +462,7 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         }
     }
     if constexpr (HAS_NEXT) {
-      if constexpr (MASK_NEXT) mask_tile<CAUSAL>(s_next, (t + 1) * kBlockN, q0, N, l32, half);
+      if constexpr (MASK_NEXT) mask_tile<CAUSAL>(s_next, (t + 1) * kBlockN, q0 + off, Nk, l32, half);
       const float mx = tile_max(s_next);
       // Lazy rescale: lanes L and L^32 agree on mx and m_ref, hence on `grow`.
       const bool grow = (mx - m_ref) * c > kRescaleLog2;
@@ -476,7 +508,7 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   // Epilogue: O = acc / l, rounded to bf16; lse = (m*c + log2 l) * ln 2.
   if (q0 + l32 >= N) return;  // a partial last query tile stores only rows < N
   const float l_tot = pair_sum(l_run);
-  const float inv = 1.0f / l_tot;
+  const float inv = (GENERAL && l_tot == 0.f) ? 0.f : 1.0f / l_tot;
   __bf16* const orow = o + head_off + (size_t)(q0 + l32) * D;
 #pragma unroll
   for (int b = 0; b < kDBlocks; ++b) {
@@ -488,7 +520,9 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * j + 4 * half) = ov;
     }
   }
-  if (half == 0) lse[(size_t)head * N + q0 + l32] = (m_ref * c + log2f(l_tot)) * kLn2;
+  if (half == 0)
+    lse[(size_t)head * N + q0 + l32] =
+        (GENERAL && l_tot == 0.f) ? -INFINITY : (m_ref * c + log2f(l_tot)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -515,47 +549,81 @@ const DeviceInfo* device_info(int dev) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-template <int D, bool CAUSAL>
-int launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-           float c, hipStream_t stream) {
-  const int n_qt = (N + Launch<D>::kBlockM - 1) / Launch<D>::kBlockM;
+template <int D, bool CAUSAL, bool GENERAL>
+int launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Nq, int Nk,
+           int off, float c, hipStream_t stream) {
+  const int n_qt = (Nq + Launch<D>::kBlockM - 1) / Launch<D>::kBlockM;
   const int grid = n_qt * BH;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL>), dim3(grid), dim3(Launch<D>::kThreads), 0, stream,
-                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                     static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, N, c);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, GENERAL>), dim3(grid), dim3(Launch<D>::kThreads), 0,
+                     stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                     static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, Nq, c, Nk, off);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+template <bool GENERAL>
+int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Nq,
+             int Nk, int d, int causal, float scale, hipStream_t s) {
+  const float c = scale * kLog2e;
+  const int off = causal ? Nk - Nq : 0;
+  if (d == 64) {
+    return causal ? launch<64, true, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, s)
+                  : launch<64, false, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, s);
+  }
+  return causal ? launch<128, true, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, s)
+                : launch<128, false, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, s);
+}
+
+// Argument checks shared by the entry points (before any HIP call).
+int check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               int B, int H, int Nq, int Nk, int d, float scale, bool* nothing) {
+  *nothing = false;
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (!(scale > 0.0f) || !isfinite(scale)) return ATTN_ERR_SCALE;
+  const int64_t bh = (int64_t)B * H;
+  if (bh > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (bh * (((int64_t)Nq + 127) / 128) > INT32_MAX) return ATTN_ERR_SHAPE;  // grid (any d)
+  if ((int64_t)Nq * d * 2 > INT32_MAX || (int64_t)Nk * d * 2 > INT32_MAX)
+    return ATTN_ERR_SHAPE;  // one head's bytes fit an int
+  if (bh == 0 || Nq == 0) {
+    *nothing = true;
+    return ATTN_OK;
+  }
+  if (!q || !o || !lse || (Nk > 0 && (!k || !v))) return ATTN_ERR_NULL;  // k, v unread if Nk = 0
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+  const DeviceInfo* info = device_info(dev);
+  if (!info || !info->gfx950) return ATTN_ERR_DEVICE;
+  return ATTN_OK;
 }
 
 }  // namespace
 
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                         int H, int N, int d, int causal, float scale, void* stream) {
-  if (B < 0 || H < 0 || N < 0) return ATTN_ERR_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
-  if (!(scale > 0.0f) || !isfinite(scale)) return ATTN_ERR_SCALE;
-  const int64_t bh = (int64_t)B * H;
-  if (bh > INT32_MAX) return ATTN_ERR_SHAPE;
-  if (bh * (((int64_t)N + 127) / 128) > INT32_MAX) return ATTN_ERR_SHAPE;  // grid (any d)
-  if ((int64_t)N * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;  // one head's bytes fit an int
-  if (bh == 0 || N == 0) return ATTN_OK;
-  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-    return ATTN_ERR_ALIGN;
+  bool nothing = false;
+  int st = check_args(q, k, v, o, lse, B, H, N, N, d, scale, &nothing);
+  if (st != ATTN_OK || nothing) return st;
+  if ((st = check_device()) != ATTN_OK) return st;
+  return dispatch<false>(q, k, v, o, lse, B * H, N, N, d, causal, scale,
+                         static_cast<hipStream_t>(stream));
+}
 
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
-  const DeviceInfo* info = device_info(dev);
-  if (!info || !info->gfx950) return ATTN_ERR_DEVICE;
-
-  const float c = scale * kLog2e;
+extern "C" int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                           int H, int Nq, int Nk, int d, int causal, float scale, void* stream) {
+  bool nothing = false;
+  int st = check_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, &nothing);
+  if (st != ATTN_OK || nothing) return st;
+  if ((st = check_device()) != ATTN_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int BH = static_cast<int>(bh);
-  if (d == 64) {
-    return causal ? launch<64, true>(q, k, v, o, lse, BH, N, c, s)
-                  : launch<64, false>(q, k, v, o, lse, BH, N, c, s);
-  }
-  return causal ? launch<128, true>(q, k, v, o, lse, BH, N, c, s)
-                : launch<128, false>(q, k, v, o, lse, BH, N, c, s);
+  if (Nq == Nk) return dispatch<false>(q, k, v, o, lse, B * H, Nq, Nk, d, causal, scale, s);
+  return dispatch<true>(q, k, v, o, lse, B * H, Nq, Nk, d, causal, scale, s);
 }
 
 extern "C" const char* attn_fwd_strerror(int status) {
@@ -573,4 +641,4 @@ extern "C" const char* attn_fwd_strerror(int status) {
   }
 }
 
-extern "C" int attn_fwd_abi_version(void) { return 1; }
+extern "C" int attn_fwd_abi_version(void) { return 2; }

@@ -80,10 +80,30 @@ int attn_fwd(const void *q, const void *k, const void *v,
              int causal, float scale,
              void *stream);
 
+/*
+ * attn_fwd_ex -- the same forward for Nq queries against Nk keys per head.
+ *
+ *   q, o     [B, H, Nq, d];  k, v  [B, H, Nk, d];  lse  [B, H, Nq].
+ *   causal   non-zero: the mask is aligned bottom-right, key j is visible to
+ *            query i iff j <= i + (Nk - Nq) (the last query sees every key;
+ *            with Nq = Nk this is attn_fwd's mask).  A row that sees no key
+ *            (Nq > Nk, causal; or Nk = 0) is written as o = 0, lse = -inf, so
+ *            that it drops out of a log-sum-exp merge of partial results.
+ *
+ * Every other argument, and ownership, errors and semantics, are as for
+ * attn_fwd (k and v may be NULL when Nk = 0: they are not read).  With
+ * Nq = Nk the call is exactly attn_fwd.
+ */
+int attn_fwd_ex(const void *q, const void *k, const void *v,
+                void *o, float *lse,
+                int B, int H, int Nq, int Nk, int d,
+                int causal, float scale,
+                void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *attn_fwd_strerror(int status);
 
-/* ABI version of this header's entry points (currently 1). */
+/* ABI version of this header's entry points (currently 2: attn_fwd_ex added). */
 int attn_fwd_abi_version(void);
 
 #ifdef __cplusplus

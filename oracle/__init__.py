@@ -65,6 +65,11 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
         u16p, u16p, u16p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double,
         ctypes.POINTER(ctypes.c_int64), i64, f64p, f64p]
     lib.attn_oracle_rows.restype = ctypes.c_int
+    if hasattr(lib, "attn_oracle_rows_ex"):
+        lib.attn_oracle_rows_ex.argtypes = [
+            u16p, u16p, u16p, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double,
+            ctypes.POINTER(ctypes.c_int64), i64, f64p, f64p]
+        lib.attn_oracle_rows_ex.restype = ctypes.c_int
     if hasattr(lib, "attn_bwd_oracle_heads"):
         lib.attn_bwd_oracle_heads.argtypes = [
             u16p, u16p, u16p, u16p, i64, i64, i64, ctypes.c_int, ctypes.c_double, i64, i64,
@@ -234,3 +239,49 @@ def backward_head_f64(q, k, v, dout, causal: bool, scale: float,
     if st != 0:
         raise RuntimeError(f"oracle failed with status {st}")
     return dq, dk, dv, delta, o, lse
+
+
+# ---------------------------------------------------------------------------
+# General shapes: Nq queries, Nk keys, bottom-right causal (attn_oracle.c)
+# ---------------------------------------------------------------------------
+
+def attention_ex(q, k, v, causal: bool, scale: float, threads: int = 1,
+                 lib: ctypes.CDLL | None = None):
+    """Oracle output for q [B,H,Nq,d] against k, v [B,H,Nk,d] (bf16 bits).
+
+    Causal masks are bottom-right aligned: key j is visible to query i iff
+    j <= i + Nk - Nq.  Rows that see no key give o = 0, lse = -inf.
+    Returns ``o`` float64 [B,H,Nq,d] and ``lse`` float64 [B,H,Nq].
+    """
+    for name, a in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(a, np.ndarray) or a.dtype != np.uint16 or a.ndim != 4:
+            raise TypeError(f"{name} must be a 4-D numpy uint16 array of bf16 bits")
+    q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+    B, H, Nq, d = q.shape
+    if k.shape != v.shape or k.shape[:2] != (B, H) or k.shape[3] != d:
+        raise ValueError("k and v must be [B, H, Nk, d] matching q's B, H and d")
+    Nk = k.shape[2]
+    lib = lib or load()
+    rows = np.arange(B * H * Nq, dtype=np.int64)
+    o = np.zeros((rows.size, d)); lse = np.zeros(rows.size)
+    threads = max(1, min(int(threads), rows.size or 1))
+    bounds = np.linspace(0, rows.size, threads + 1).astype(np.int64)
+
+    def run(part):
+        lo, hi = int(bounds[part]), int(bounds[part + 1])
+        if hi <= lo:
+            return 0
+        sub = rows[lo:hi]
+        return lib.attn_oracle_rows_ex(
+            _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
+            B, H, Nq, Nk, d, int(bool(causal)), float(scale), _ptr(sub, ctypes.c_int64), hi - lo,
+            _ptr(o[lo:hi], ctypes.c_double), _ptr(lse[lo:hi], ctypes.c_double))
+
+    if threads == 1:
+        statuses = [run(0)]
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as pool:
+            statuses = list(pool.map(run, range(threads)))
+    if any(s != 0 for s in statuses):
+        raise RuntimeError(f"oracle failed with status {statuses}")
+    return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)

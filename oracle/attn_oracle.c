@@ -124,3 +124,80 @@ int attn_oracle_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     free(scores);
     return status;
 }
+
+/*
+ * General shapes: Nq queries against Nk keys per head.  q and o are
+ * [B,H,Nq,d], k and v are [B,H,Nk,d].  Causal masks are aligned bottom-right
+ * (the convention for a block of queries that ends where the keys end): key
+ * j is visible to query i iff j <= i + (Nk - Nq); with Nq = Nk this is the
+ * mask of attn_oracle_row.  A row that sees no key (possible when Nq > Nk)
+ * has no softmax; it is defined here as o = 0 and lse = -infinity, the
+ * values that make it vanish from a log-sum-exp merge of partial results.
+ * `scores` is caller scratch of at least Nk doubles.
+ */
+int attn_oracle_row_ex(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                       int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                       int causal, double scale,
+                       int64_t b, int64_t h, int64_t i,
+                       double *o_row, double *lse_out, double *scores)
+{
+    if (!q || !k || !v || !o_row || !lse_out || !scores) return ORACLE_ERR_ARG;
+    if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return ORACLE_ERR_ARG;
+    if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= Nq) return ORACLE_ERR_ARG;
+
+    const uint16_t *qi = q + ((b * H + h) * Nq + i) * d;
+    const uint16_t *kh = k + (b * H + h) * Nk * d;
+    const uint16_t *vh = v + (b * H + h) * Nk * d;
+    int64_t nvis = Nk;
+    if (causal) {
+        const int64_t last = i + (Nk - Nq);      /* last visible key */
+        nvis = last < 0 ? 0 : (last + 1 < Nk ? last + 1 : Nk);
+    }
+    for (int64_t t = 0; t < d; ++t) o_row[t] = 0.0;
+    if (nvis == 0) {
+        *lse_out = -INFINITY;
+        return ORACLE_OK;
+    }
+
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nvis; ++j) {
+        double dot = 0.0;
+        for (int64_t t = 0; t < d; ++t)
+            dot += widen_bf16(qi[t]) * widen_bf16(kh[j * d + t]);
+        scores[j] = scale * dot;
+        if (scores[j] > m) m = scores[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < nvis; ++j) {
+        const double w = exp(scores[j] - m);
+        l += w;
+        for (int64_t t = 0; t < d; ++t)
+            o_row[t] += w * widen_bf16(vh[j * d + t]);
+    }
+    for (int64_t t = 0; t < d; ++t) o_row[t] /= l;
+    *lse_out = m + log(l);
+    return ORACLE_OK;
+}
+
+/* Rows r = (b*H + h)*Nq + i of the general-shape problem; see above. */
+int attn_oracle_rows_ex(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                        int causal, double scale,
+                        const int64_t *rows, int64_t nrows,
+                        double *o_out, double *lse_out)
+{
+    if (!rows || !o_out || !lse_out || nrows < 0 || Nk <= 0 || Nq <= 0) return ORACLE_ERR_ARG;
+    double *scores = (double *)malloc((size_t)Nk * sizeof(double));
+    if (!scores) return ORACLE_ERR_NOMEM;
+    int status = ORACLE_OK;
+    for (int64_t n = 0; n < nrows && status == ORACLE_OK; ++n) {
+        const int64_t r = rows[n];
+        if (r < 0 || r >= B * H * Nq) { status = ORACLE_ERR_ARG; break; }
+        const int64_t bh = r / Nq;
+        status = attn_oracle_row_ex(q, k, v, B, H, Nq, Nk, d, causal, scale,
+                                    bh / H, bh % H, r % Nq,
+                                    o_out + n * d, lse_out + n, scores);
+    }
+    free(scores);
+    return status;
+}

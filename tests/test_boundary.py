@@ -40,7 +40,7 @@ def declared_functions():
 def test_headers_declare_the_entry_points():
     assert [os.path.basename(h) for h in HEADERS] == ["attn_bwd.h", "attn_fwd.h"]
     assert declared_functions() == ["attn_bwd", "attn_fwd", "attn_fwd_abi_version",
-                                    "attn_fwd_strerror"]
+                                    "attn_fwd_ex", "attn_fwd_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -57,7 +57,7 @@ def test_status_codes_match_header(lib):
         msg = af.attn_fwd_strerror(value)
         assert msg and msg != "unknown status"
     assert af.attn_fwd_strerror(12345) == "unknown status"
-    assert lib.attn_fwd_abi_version() == 1
+    assert lib.attn_fwd_abi_version() == 2
 
 
 def call(B=2, H=3, N=256, d=128, causal=0, scale=0.088, q=FAKE, k=FAKE, v=FAKE, o=FAKE,
@@ -158,3 +158,30 @@ def test_python_bwd_binding_rejects_cpu_tensors():
     lse = torch.zeros(1, 1, 64)
     with pytest.raises(ValueError):
         af.attn_bwd(x, x, x, x, lse, x)
+
+
+def call_ex(B=2, H=3, Nq=100, Nk=300, d=128, causal=1, scale=0.088, q=FAKE, k=FAKE, v=FAKE,
+            o=FAKE, lse=FAKE):
+    return af.attn_fwd_ex_raw(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Nq=-1), af.Status.ERR_SHAPE),
+    (dict(Nk=-1), af.Status.ERR_SHAPE),
+    (dict(d=96), af.Status.ERR_HEAD_DIM),
+    (dict(scale=-1.0), af.Status.ERR_SCALE),
+    (dict(Nk=1 << 24), af.Status.ERR_SHAPE),
+    (dict(Nq=1 << 24), af.Status.ERR_SHAPE),
+    (dict(q=0), af.Status.ERR_NULL),
+    (dict(k=0), af.Status.ERR_NULL),
+    (dict(lse=0), af.Status.ERR_NULL),
+    (dict(v=FAKE + 8), af.Status.ERR_ALIGN),
+    (dict(o=FAKE + 2), af.Status.ERR_ALIGN),
+])
+def test_ex_rejects(lib, kw, status):
+    assert call_ex(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(Nq=0), dict(B=0), dict(Nq=0, q=0, k=0, v=0, o=0, lse=0)])
+def test_ex_empty_problem_is_a_noop(lib, kw):
+    assert call_ex(**kw) == af.Status.OK

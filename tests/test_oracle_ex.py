@@ -1,0 +1,144 @@
+"""The general-shape forward oracle (Nq queries, Nk keys, bottom-right causal)
+against facts fixed by mathematics, and mutations of it against those pins.
+
+Pins: equality with the (pinned) square oracle when Nq = Nk; scipy softmax /
+logsumexp over numpy fp64 scores with the bottom-right mask built by hand;
+closed forms for rows that see no key (o = 0, lse = -inf) or exactly one key
+(o = v_0); the causal last row sees every key; and the log-sum-exp merge of
+the results over two key ranges equals the result over their union.
+"""
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+from attention_attn_fwd_08_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits
+
+
+def _bits(rng, *shape):
+    return f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+
+
+def _f(bits):
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _reference(q, k, v, causal, scale):
+    """numpy scores + scipy softmax with the bottom-right mask; empty rows 0/-inf."""
+    qf, kf, vf = _f(q), _f(k), _f(v)
+    Nq, Nk = q.shape[2], k.shape[2]
+    s = scale * np.einsum("bhid,bhjd->bhij", qf, kf)
+    if causal:
+        i = np.arange(Nq)[:, None]
+        j = np.arange(Nk)[None, :]
+        s = np.where(j <= i + (Nk - Nq), s, -np.inf)
+    empty = np.all(np.isneginf(s), axis=-1)
+    s_safe = np.where(empty[..., None], 0.0, s)
+    p = scipy.special.softmax(s_safe, axis=-1)
+    o = np.einsum("bhij,bhjd->bhid", p, vf)
+    lse = scipy.special.logsumexp(s_safe, axis=-1)
+    o[empty] = 0.0
+    lse[empty] = -np.inf
+    return o, lse
+
+
+def pin_ex_square_is_the_forward_oracle(lib):
+    rng = np.random.default_rng(21)
+    q, k, v = (_bits(rng, 1, 2, 23, 8) for _ in range(3))
+    for causal in (False, True):
+        o1, l1 = oracle.attention(q, k, v, causal, 0.4, lib=lib)
+        o2, l2 = oracle.attention_ex(q, k, v, causal, 0.4, lib=lib)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2), f"square case (causal={causal})"
+
+
+def pin_ex_scipy(lib):
+    rng = np.random.default_rng(22)
+    for Nq, Nk in ((5, 13), (13, 5), (1, 9), (9, 1), (7, 7)):
+        q = _bits(rng, 2, 1, Nq, 6)
+        k, v = _bits(rng, 2, 1, Nk, 6), _bits(rng, 2, 1, Nk, 6)
+        for causal in (False, True):
+            o, l = oracle.attention_ex(q, k, v, causal, 0.45, lib=lib)
+            o_ref, l_ref = _reference(q, k, v, causal, 0.45)
+            assert np.allclose(o, o_ref, rtol=1e-12, atol=1e-12), f"o Nq={Nq} Nk={Nk} c={causal}"
+            fin = np.isfinite(l_ref)
+            assert np.array_equal(fin, np.isfinite(l)), f"lse finiteness Nq={Nq} Nk={Nk}"
+            assert np.allclose(l[fin], l_ref[fin], rtol=1e-12, atol=1e-12), f"lse Nq={Nq} Nk={Nk}"
+            assert np.all(np.isneginf(l[~fin])), "empty rows have lse = -inf"
+
+
+def pin_ex_empty_and_single_key_rows(lib):
+    rng = np.random.default_rng(23)
+    Nq, Nk, d, scale = 9, 4, 5, 0.7
+    q, k, v = _bits(rng, 1, 1, Nq, d), _bits(rng, 1, 1, Nk, d), _bits(rng, 1, 1, Nk, d)
+    o, l = oracle.attention_ex(q, k, v, True, scale, lib=lib)
+    n_empty = Nq - Nk
+    assert np.all(o[0, 0, :n_empty] == 0.0), "rows with no visible key: o = 0"
+    assert np.all(np.isneginf(l[0, 0, :n_empty])), "rows with no visible key: lse = -inf"
+    assert np.allclose(o[0, 0, n_empty], _f(v)[0, 0, 0], atol=1e-15), "one visible key: o = v_0"
+    s00 = scale * float(_f(q)[0, 0, n_empty] @ _f(k)[0, 0, 0])
+    assert abs(l[0, 0, n_empty] - s00) < 1e-13, "one visible key: lse = s"
+
+
+def pin_ex_causal_last_row_sees_all(lib):
+    rng = np.random.default_rng(24)
+    q, k, v = _bits(rng, 1, 2, 6, 4), _bits(rng, 1, 2, 11, 4), _bits(rng, 1, 2, 11, 4)
+    oc, lc = oracle.attention_ex(q, k, v, True, 0.5, lib=lib)
+    on, ln = oracle.attention_ex(q, k, v, False, 0.5, lib=lib)
+    assert np.allclose(oc[:, :, -1], on[:, :, -1], atol=1e-14), "last row o"
+    assert np.allclose(lc[:, :, -1], ln[:, :, -1], atol=1e-14), "last row lse"
+
+
+def pin_ex_merge_over_key_ranges(lib):
+    """softmax over keys A u B from the two partial results and their lse."""
+    rng = np.random.default_rng(25)
+    Nq, Nk, c = 6, 14, 5
+    q, k, v = _bits(rng, 1, 1, Nq, 4), _bits(rng, 1, 1, Nk, 4), _bits(rng, 1, 1, Nk, 4)
+    o, l = oracle.attention_ex(q, k, v, False, 0.6, lib=lib)
+    o1, l1 = oracle.attention_ex(q, k[:, :, :c].copy(), v[:, :, :c].copy(), False, 0.6, lib=lib)
+    o2, l2 = oracle.attention_ex(q, k[:, :, c:].copy(), v[:, :, c:].copy(), False, 0.6, lib=lib)
+    lm = np.logaddexp(l1, l2)
+    om = np.exp(l1 - lm)[..., None] * o1 + np.exp(l2 - lm)[..., None] * o2
+    assert np.allclose(lm, l, atol=1e-13), "merged lse"
+    assert np.allclose(om, o, atol=1e-13), "merged o"
+
+
+ALL_EX_PINS = [pin_ex_square_is_the_forward_oracle, pin_ex_scipy, pin_ex_empty_and_single_key_rows,
+               pin_ex_causal_last_row_sees_all, pin_ex_merge_over_key_ranges]
+
+
+@pytest.mark.parametrize("pin", ALL_EX_PINS, ids=lambda p: p.__name__)
+def test_ex_pin_holds(pin):
+    pin(oracle.load())
+
+
+MUTANTS = {
+    "top-left instead of bottom-right": ("const int64_t last = i + (Nk - Nq);", "const int64_t last = i;"),
+    "causal bound off by one": ("nvis = last < 0 ? 0 : (last + 1 < Nk ? last + 1 : Nk);",
+                                "nvis = last < 0 ? 0 : (last < Nk ? last : Nk);"),
+    "key head stride uses Nq": ("const uint16_t *kh = k + (b * H + h) * Nk * d;",
+                                "const uint16_t *kh = k + (b * H + h) * Nq * d;"),
+    "query stride uses Nk": ("const uint16_t *qi = q + ((b * H + h) * Nq + i) * d;",
+                             "const uint16_t *qi = q + ((b * H + h) * Nk + i) * d;"),
+    "empty row lse zero": ("        *lse_out = -INFINITY;\n        return ORACLE_OK;",
+                           "        *lse_out = 0.0;\n        return ORACLE_OK;"),
+    "row index from Nk": ("bh / H, bh % H, r % Nq,", "bh / H, bh % H, r % Nk,"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_ex_mutant_is_caught(name, tmp_path):
+    before, after = MUTANTS[name]
+    src = open(oracle.SOURCE).read()
+    assert src.count(before) == 1, f"anchor for '{name}' not found exactly once"
+    mutated = tmp_path / "attn_oracle_mutant.c"
+    mutated.write_text(src.replace(before, after))
+    lib_path = str(tmp_path / "libmutant.so")
+    oracle.build(str(mutated), lib_path)
+    lib = oracle.load(lib_path)
+    caught = []
+    for pin in ALL_EX_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, RuntimeError, FloatingPointError, ValueError) as e:
+            caught.append((pin.__name__, str(e)[:80]))
+    assert caught, f"no pin detects the mutation '{name}'"
