@@ -26,6 +26,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "attn_bwd.h"
 
 namespace {
@@ -94,26 +96,28 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(size_t)(__attribute__((address_space(3))) const unsigned char*)p;
 }
 
-// Copy rows [row0, row0 + kTile) of a [N, D] bf16 matrix into a swizzled LDS
-// tile (rows past N read as zeros).  Every wave copies kLoads slices.
-template <int D>
+// Copy rows [row0, row0 + ROWS) of a [N, D] bf16 matrix into a swizzled LDS
+// tile (rows past N read as zeros).  Every wave copies its share of slices.
+template <int D, int ROWS = kTile>
 __device__ __forceinline__ void copy_tile(const __bf16* mat, int N, int row0, unsigned tile_lds,
                                           int wave, int lane) {
   using G = Geo<D>;
   constexpr int kChunks = D / 8;
+  constexpr int kLoads = ROWS / (G::kRowsPerLoad * kWaves);
   const i32x4 rsrc = make_rsrc(mat + (size_t)row0 * D, (N - row0) * G::kRowBytes);
 #pragma unroll
-  for (int it = 0; it < G::kLoads; ++it) {
-    const int r = (wave * G::kLoads + it) * G::kRowsPerLoad + lane / kChunks;
+  for (int it = 0; it < kLoads; ++it) {
+    const int r = (wave * kLoads + it) * G::kRowsPerLoad + lane / kChunks;
     const int voff = r * G::kRowBytes + (((lane % kChunks) ^ swz<D>(r)) << 4);
-    load16_to_lds(rsrc, voff, tile_lds + (wave * G::kLoads + it) * G::kRowsPerLoad * G::kRowBytes);
+    load16_to_lds(rsrc, voff, tile_lds + (wave * kLoads + it) * G::kRowsPerLoad * G::kRowBytes);
   }
 }
 
-// Copy kTile floats [row0, row0 + kTile) of a length-N vector into LDS (lanes
-// 0..15 of one wave; entries past N read as zeros).
+// Copy ROWS floats [row0, row0 + ROWS) of a length-N vector into LDS (lanes
+// 0..ROWS/4-1 of one wave; entries past N read as zeros).
+template <int ROWS = kTile>
 __device__ __forceinline__ void copy_vec(const float* vec, int N, int row0, unsigned dst, int lane) {
-  if (lane < kTile / 4) {
+  if (lane < ROWS / 4) {
     const i32x4 rsrc = make_rsrc(vec + row0, (N - row0) * 4);
     load16_to_lds(rsrc, lane * 16, dst);
   }
@@ -202,8 +206,14 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   using G = Geo<D>;
   constexpr int kSteps = G::kSteps;
   constexpr int kDBlocks = G::kDBlocks;
-  constexpr int kTileBytes = G::kTileBytes;
-  constexpr int kStageBytes = 2 * kTileBytes + 2 * kTile * 4;  // Q, dO, lse, delta
+  // d=128 (one wave per SIMD): 128-query tiles, and the next block's S/dP
+  // MFMAs are issued before this block's exponentials.  d=64 (several waves
+  // per SIMD hide each other): 64-query tiles, blocks one after another.
+  constexpr bool kPipe = D == 128;
+  constexpr int kQT = kPipe ? 128 : 64;       // queries per streamed tile
+  constexpr int kQBlocks = kQT / kRows;       // 32-query blocks per tile
+  constexpr int kTileBytes = kQT * G::kRowBytes;
+  constexpr int kStageBytes = 2 * kTileBytes + 2 * kQT * 4;  // Q, dO, lse, delta
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStageBytes];
 
   const int tid = threadIdx.x;
@@ -254,17 +264,17 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       for (int h = 0; h < 2; ++h) tro[cc][b][h] = tr_off<D>(lane, h, b, cc);
 
   // Query tiles that see at least one key of the block.
-  const int qt_first = CAUSAL ? (kb * kBlock) / kTile : 0;
-  const int n_qt = (N + kTile - 1) / kTile;
+  const int qt_first = CAUSAL ? (kb * kBlock) / kQT : 0;
+  const int n_qt = (N + kQT - 1) / kQT;
   auto stage_ptr = [&](int s) __attribute__((always_inline)) { return smem + s * kStageBytes; };
   auto issue = [&](int qt, int s) __attribute__((always_inline)) {
     unsigned char* st_base = stage_ptr(s);
-    const int row0 = qt * kTile;
-    copy_tile<D>(qh, N, row0, lds_addr(st_base), wave, lane);
-    copy_tile<D>(doh, N, row0, lds_addr(st_base + kTileBytes), wave, lane);
+    const int row0 = qt * kQT;
+    copy_tile<D, kQT>(qh, N, row0, lds_addr(st_base), wave, lane);
+    copy_tile<D, kQT>(doh, N, row0, lds_addr(st_base + kTileBytes), wave, lane);
     if (wave == 0) {
-      copy_vec(lseh, N, row0, lds_addr(st_base + 2 * kTileBytes), lane);
-      copy_vec(dlth, N, row0, lds_addr(st_base + 2 * kTileBytes + kTile * 4), lane);
+      copy_vec<kQT>(lseh, N, row0, lds_addr(st_base + 2 * kTileBytes), lane);
+      copy_vec<kQT>(dlth, N, row0, lds_addr(st_base + 2 * kTileBytes + kQT * 4), lane);
     }
   };
   if (qt_first < n_qt) issue(qt_first, 0);
@@ -277,17 +287,13 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const unsigned char* const qt_lds = stage_ptr(s);
     const unsigned char* const dot_lds = qt_lds + kTileBytes;
     const float* const lse_lds = reinterpret_cast<const float*>(qt_lds + 2 * kTileBytes);
-    const float* const dlt_lds = lse_lds + kTile;
+    const float* const dlt_lds = lse_lds + kQT;
 
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int qrow0 = qt * kTile + qb * kRows;
-      if (CAUSAL && qrow0 + kRows - 1 < key0) continue;  // every query precedes every key
+    // S = Q K^T and dP = dO V^T of query block qb: [queries, keys]; lane =
+    // key, register r = query 8*(r/4) + 4*(L/32) + r%4 of the block.
+    auto sdp = [&](int qb, f32x16& sacc, f32x16& pacc) __attribute__((always_inline)) {
       const unsigned char* const qa = qt_lds + qb * kRows * G::kRowBytes;
       const unsigned char* const da = dot_lds + qb * kRows * G::kRowBytes;
-      // S = Q K^T and dP = dO V^T: [queries, keys]; lane = key, register r =
-      // query 8*(r/4) + 4*(L/32) + r%4 of the block.
-      f32x16 sacc, pacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[r] = pacc[r] = 0.f;
 #pragma unroll
@@ -295,9 +301,12 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         sacc = mfma(*reinterpret_cast<const bf16x8*>(qa + ro[st]), kf[st], sacc);
         pacc = mfma(*reinterpret_cast<const bf16x8*>(da + ro[st]), vf[st], pacc);
       }
-      // P = 2^(s*c - lse*log2 e), dS = P (dP - delta); masked entries are 0.
-      const bool partial = (CAUSAL && qrow0 < key0 + kRows - 1) || qrow0 + kRows > N;
-      bf16x8 pb[2], sb[2];
+    };
+    // P = 2^(s*c - lse*log2 e) and dS = P (dP - delta), as bf16 B operands;
+    // with MASK, entries a query does not see are 0.
+    auto soft = [&](auto mask_tag, int qb, const f32x16& sacc, const f32x16& pacc, bf16x8(&pb)[2],
+                    bf16x8(&sb)[2]) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int qi = qb * kRows + 8 * g + 4 * half;  // tile row of registers 4g..4g+3
@@ -307,17 +316,20 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         for (int j = 0; j < 4; ++j) {
           const int r = 4 * g + j;
           float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -l4[j] * kLog2e));
-          if (partial) {
-            const int query = qt * kTile + qi + j;
+          if constexpr (MASK) {
+            const int query = qt * kQT + qi + j;
             const bool vis = CAUSAL ? (key0 + l32 <= query && query < N) : (query < N);
             p = vis ? p : 0.f;
           }
-          const float ds = p * (pacc[r] - d4[j]);
           pb[r >> 3][r & 7] = (__bf16)p;
-          sb[r >> 3][r & 7] = (__bf16)ds;
+          sb[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - d4[j]));
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-query steps.
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-query steps.
+    auto pv = [&](int qb, const bf16x8(&pb)[2], const bf16x8(&sb)[2]) __attribute__((always_inline)) {
+      const unsigned char* const qa = qt_lds + qb * kRows * G::kRowBytes;
+      const unsigned char* const da = dot_lds + qb * kRows * G::kRowBytes;
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
@@ -325,6 +337,35 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           dvt[b] = mfma(read_tr(da, tro[cc][b][0], tro[cc][b][1]), pb[cc], dvt[b]);
           dkt[b] = mfma(read_tr(qa, tro[cc][b][0], tro[cc][b][1]), sb[cc], dkt[b]);
         }
+    };
+
+    const int qrow_first = qt * kQT;
+    const bool interior = (!CAUSAL || qrow_first >= key0 + kRows - 1) && qrow_first + kQT <= N;
+    if (kPipe && interior) {
+      // Every block fully visible: the next block's S and dP go to the MFMA
+      // pipe before this block's exponentials, which then overlap them.
+      f32x16 sa[2], pa[2];
+      sdp(0, sa[0], pa[0]);
+#pragma unroll
+      for (int qb = 0; qb < kQBlocks; ++qb) {
+        if (qb + 1 < kQBlocks) sdp(qb + 1, sa[(qb + 1) & 1], pa[(qb + 1) & 1]);
+        bf16x8 pb[2], sb[2];
+        soft(std::false_type{}, qb, sa[qb & 1], pa[qb & 1], pb, sb);
+        pv(qb, pb, sb);
+      }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < kQBlocks; ++qb) {
+        const int qrow0 = qrow_first + qb * kRows;
+        if (CAUSAL && qrow0 + kRows - 1 < key0) continue;  // every query precedes every key
+        if (qrow0 >= N) continue;
+        f32x16 sacc, pacc;
+        sdp(qb, sacc, pacc);
+        bf16x8 pb[2], sb[2];
+        if (interior) soft(std::false_type{}, qb, sacc, pacc, pb, sb);
+        else soft(std::true_type{}, qb, sacc, pacc, pb, sb);
+        pv(qb, pb, sb);
+      }
     }
   }
 
