@@ -23,7 +23,8 @@ import math
 import os
 import threading
 
-__all__ = ["attn_fwd", "attn_fwd_raw", "attn_fwd_ex", "attn_fwd_ex_raw", "attn_bwd",
+__all__ = ["attn_fwd", "attn_fwd_raw", "attn_fwd_ex", "attn_fwd_ex_raw", "attn_fwd_splitkv",
+           "attn_fwd_splitkv_raw", "splitkv_splits", "attn_bwd",
            "attn_bwd_raw", "attn_fwd_strerror", "load_library", "LIBRARY", "Status", "AttnError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -80,6 +81,9 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.attn_fwd_abi_version.restype = ctypes.c_int
     lib.attn_fwd_ex.argtypes = [vp] * 5 + [ctypes.c_int] * 6 + [ctypes.c_float, vp]
     lib.attn_fwd_ex.restype = ctypes.c_int
+    lib.attn_fwd_splitkv.argtypes = ([vp] * 5 + [ctypes.c_int] * 6 + [ctypes.c_float, ctypes.c_int]
+                                     + [vp] * 3)
+    lib.attn_fwd_splitkv.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [vp] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float, vp]
     lib.attn_bwd.restype = ctypes.c_int
     return lib
@@ -249,6 +253,68 @@ def attn_fwd_ex(q, k, v, causal: bool = False, scale: float | None = None, out=N
         stream = torch.cuda.current_stream(q.device).cuda_stream
         status = attn_fwd_ex_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                  lse.data_ptr(), B, H, Nq, Nk, d, causal, scale, stream)
+    if status != Status.OK:
+        raise AttnError(status, attn_fwd_strerror(status))
+    return out, lse
+
+
+def attn_fwd_splitkv_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
+                         B: int, H: int, Nq: int, Nk: int, d: int, causal: bool, scale: float,
+                         n_splits: int, o_part_ptr: int, lse_part_ptr: int, stream: int = 0) -> int:
+    """Call attn_fwd_splitkv with raw integer addresses; returns the status."""
+    lib = load_library()
+    return lib.attn_fwd_splitkv(q_ptr or None, k_ptr or None, v_ptr or None, o_ptr or None,
+                                lse_ptr or None, int(B), int(H), int(Nq), int(Nk), int(d),
+                                int(bool(causal)), float(scale), int(n_splits),
+                                o_part_ptr or None, lse_part_ptr or None, stream or None)
+
+
+def splitkv_splits(B: int, H: int, Nq: int, Nk: int, d: int, cus: int = 256) -> int:
+    """A split count that gives about two workgroups per compute unit, with at
+    least 256 keys per split (the library rounds splits to 64-key tiles)."""
+    per_wg_queries = 256 if d == 128 else 128
+    wgs = B * H * ((Nq + per_wg_queries - 1) // per_wg_queries)
+    want = max(1, (2 * cus + max(wgs, 1) - 1) // max(wgs, 1))
+    return int(max(1, min(want, Nk // 256 if Nk >= 256 else 1)))
+
+
+def attn_fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
+                     n_splits: int | None = None, out=None, lse=None, o_part=None, lse_part=None):
+    """:func:`attn_fwd_ex` computed over ``n_splits`` key ranges and merged.
+
+    ``o_part`` (float32 [n_splits, B, H, Nq, d]) and ``lse_part`` (float32
+    [n_splits, B, H, Nq]) are the workspace; they are allocated here when not
+    given.  ``n_splits=None`` picks :func:`splitkv_splits`.
+    """
+    import torch
+
+    _check_bf16("q", q, None, None)
+    B, H, Nq, d = q.shape
+    _check_bf16("k", k, None, q.device)
+    if k.shape[:2] != (B, H) or k.shape[3] != d:
+        raise ValueError("k must be [B, H, Nk, d] with q's B, H and d")
+    _check_bf16("v", v, k.shape, q.device)
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if n_splits is None:
+        n_splits = splitkv_splits(B, H, Nq, Nk, d)
+    out = torch.empty_like(q) if out is None else out
+    _check_bf16("out", out, q.shape, q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_f32("lse", lse, (B, H, Nq), q.device)
+    if o_part is None:
+        o_part = torch.empty((n_splits, B, H, Nq, d), dtype=torch.float32, device=q.device)
+    _check_f32("o_part", o_part, (n_splits, B, H, Nq, d), q.device)
+    if lse_part is None:
+        lse_part = torch.empty((n_splits, B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_f32("lse_part", lse_part, (n_splits, B, H, Nq), q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        status = attn_fwd_splitkv_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      lse.data_ptr(), B, H, Nq, Nk, d, causal, scale, n_splits,
+                                      o_part.data_ptr(), lse_part.data_ptr(), stream)
     if status != Status.OK:
         raise AttnError(status, attn_fwd_strerror(status))
     return out, lse

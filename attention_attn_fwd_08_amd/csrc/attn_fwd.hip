@@ -57,6 +57,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -224,14 +225,22 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
 // N is the number of queries.  GENERAL: the keys number Nk (not N) and a
 // causal mask is offset by `off` (key j visible to query i iff j <= i + off);
 // rows that see no key get o = 0 and lse = -inf.  Otherwise Nk = N, off = 0
-// and every row sees key 0.
-template <int D, bool CAUSAL, bool GENERAL>
+// and every row sees key 0.  SPLIT (implies GENERAL): workgroup row
+// blockIdx.y takes only keys [y*kv_chunk, (y+1)*kv_chunk) and writes its
+// normalised partial O (fp32) and partial lse to o_part / lse_part, laid out
+// [split, head, query, d] and [split, head, query]; a merge kernel combines
+// the splits.
+template <int D, bool CAUSAL, bool GENERAL, bool SPLIT = false>
 __global__ __launch_bounds__(Launch<D>::kThreads, Launch<D>::kMinBlocks)  // <= 256 registers
 void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, __bf16* __restrict__ o,
-                     float* __restrict__ lse, int N, float c, int nk_arg, int off_arg) {
-  const int Nk = GENERAL ? nk_arg : N;
-  const int off = GENERAL ? off_arg : 0;
+                     float* __restrict__ lse, int N, float c, int nk_arg, int off_arg,
+                     int kv_chunk, float* __restrict__ o_part, float* __restrict__ lse_part) {
+  static_assert(!SPLIT || GENERAL, "a split is a general-shape problem");
+  const int Nk_all = GENERAL ? nk_arg : N;
+  const int kv_begin = SPLIT ? (int)blockIdx.y * kv_chunk : 0;  // first key of this split
+  const int Nk = SPLIT ? min(kv_chunk, Nk_all - kv_begin) : Nk_all;
+  const int off = GENERAL ? off_arg - kv_begin : 0;
   using T = Tile<D>;
   constexpr int kRowBytes = T::kRowBytes;
   constexpr int kChunksPerRow = D / 8;
@@ -267,7 +276,9 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int qt = CAUSAL ? n_qt - 1 - lid % n_qt : lid % n_qt;
 
   const size_t head_off = (size_t)head * N * D;
-  const size_t kv_head_off = (size_t)head * Nk * D;
+  const size_t kv_head_off = ((size_t)head * Nk_all + kv_begin) * D;
+  // SPLIT: this row's slot in the partial results.
+  const size_t part_row0 = SPLIT ? ((size_t)blockIdx.y * (grid / n_qt) + head) * N : 0;
   const __bf16* const qh = q + head_off;
   const __bf16* const kh = k + kv_head_off;
   const __bf16* const vh = v + kv_head_off;
@@ -293,13 +304,23 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     if (n_tiles <= 0) {  // no query of the workgroup sees a key
       const int qrow = q0 + l32;
       if (qrow < N) {
-        __bf16* const orow = o + head_off + (size_t)qrow * D;
+        if constexpr (SPLIT) {
+          float* const prow = o_part + (part_row0 + qrow) * D;
 #pragma unroll
-        for (int b = 0; b < D / 32; ++b)
+          for (int b = 0; b < D / 32; ++b)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * j + 4 * half) = bf16x4{0, 0, 0, 0};
-        if (half == 0) lse[(size_t)head * N + qrow] = -INFINITY;
+            for (int j = 0; j < 4; ++j)
+              *reinterpret_cast<f32x4*>(prow + 32 * b + 8 * j + 4 * half) = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (half == 0) lse_part[part_row0 + qrow] = -INFINITY;
+        } else {
+          __bf16* const orow = o + head_off + (size_t)qrow * D;
+#pragma unroll
+          for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * j + 4 * half) = bf16x4{0, 0, 0, 0};
+          if (half == 0) lse[(size_t)head * N + qrow] = -INFINITY;
+        }
       }
       return;
     }
@@ -509,6 +530,19 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   if (q0 + l32 >= N) return;  // a partial last query tile stores only rows < N
   const float l_tot = pair_sum(l_run);
   const float inv = (GENERAL && l_tot == 0.f) ? 0.f : 1.0f / l_tot;
+  const float row_lse = (GENERAL && l_tot == 0.f) ? -INFINITY : (m_ref * c + log2f(l_tot)) * kLn2;
+  if constexpr (SPLIT) {
+    float* const prow = o_part + (part_row0 + q0 + l32) * D;
+#pragma unroll
+    for (int b = 0; b < kDBlocks; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(prow + 32 * b + 8 * j + 4 * half) =
+            f32x4{acc[b][4 * j] * inv, acc[b][4 * j + 1] * inv, acc[b][4 * j + 2] * inv,
+                  acc[b][4 * j + 3] * inv};
+    if (half == 0) lse_part[part_row0 + q0 + l32] = row_lse;
+    return;
+  }
   __bf16* const orow = o + head_off + (size_t)(q0 + l32) * D;
 #pragma unroll
   for (int b = 0; b < kDBlocks; ++b) {
@@ -520,9 +554,40 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * j + 4 * half) = ov;
     }
   }
-  if (half == 0)
-    lse[(size_t)head * N + q0 + l32] =
-        (GENERAL && l_tot == 0.f) ? -INFINITY : (m_ref * c + log2f(l_tot)) * kLn2;
+  if (half == 0) lse[(size_t)head * N + q0 + l32] = row_lse;
+}
+
+// Merge of the splits of one row: lse = ln sum_s exp(lse_s) and
+// O = sum_s exp(lse_s - lse) O_s (rows no split sees: O = 0, lse = -inf).
+// D/4 threads per row, four features each.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ o_part,
+                                                         const float* __restrict__ lse_part,
+                                                         __bf16* __restrict__ o,
+                                                         float* __restrict__ lse, long long rows,
+                                                         int n_splits) {
+  constexpr int kPerRow = D / 4;
+  const long long row = (long long)blockIdx.x * (256 / kPerRow) + threadIdx.x / kPerRow;
+  const int f = (threadIdx.x % kPerRow) * 4;
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) m = fmaxf(m, lse_part[(size_t)s * rows + row]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < n_splits; ++s) {
+      const float w = __expf(lse_part[(size_t)s * rows + row] - m);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(o_part + ((size_t)s * rows + row) * D + f);
+      acc += w * x;
+      wsum += w;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  bf16x4 out;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) out[r] = (__bf16)(acc[r] * inv);
+  *reinterpret_cast<bf16x4*>(o + row * D + f) = out;
+  if (f == 0) lse[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -556,7 +621,25 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
   const int grid = n_qt * BH;
   hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, GENERAL>), dim3(grid), dim3(Launch<D>::kThreads), 0,
                      stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                     static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, Nq, c, Nk, off);
+                     static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, Nq, c, Nk, off, 0,
+                     nullptr, nullptr);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+template <int D, bool CAUSAL>
+int launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Nq,
+                 int Nk, int off, float c, int n_splits, int chunk, float* o_part, float* lse_part,
+                 hipStream_t stream) {
+  const int n_qt = (Nq + Launch<D>::kBlockM - 1) / Launch<D>::kBlockM;
+  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, true, true>), dim3(n_qt * BH, n_splits),
+                     dim3(Launch<D>::kThreads), 0, stream, static_cast<const __bf16*>(q),
+                     static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+                     static_cast<__bf16*>(o), lse, Nq, c, Nk, off, chunk, o_part, lse_part);
+  const long long rows = (long long)BH * Nq;
+  constexpr int kRowsPerBlock = 256 / (D / 4);
+  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+                     dim3(256), 0, stream, o_part, lse_part, static_cast<__bf16*>(o), lse, rows,
+                     n_splits);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -626,6 +709,37 @@ extern "C" int attn_fwd_ex(const void* q, const void* k, const void* v, void* o,
   return dispatch<true>(q, k, v, o, lse, B * H, Nq, Nk, d, causal, scale, s);
 }
 
+extern "C" int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                                int n_splits, float* o_part, float* lse_part, void* stream) {
+  bool nothing = false;
+  int st = check_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, &nothing);
+  if (st != ATTN_OK) return st;
+  if (n_splits < 1) return ATTN_ERR_SHAPE;
+  if (nothing) return ATTN_OK;
+  // Splits of whole 64-key tiles; the grid's second dimension counts them.
+  const int64_t chunk64 = ((int64_t)Nk + n_splits - 1) / n_splits;
+  const int chunk = (int)(((chunk64 + 63) / 64) * 64);
+  const int used = Nk > 0 ? (int)(((int64_t)Nk + chunk - 1) / chunk) : 0;
+  if (used > 65535) return ATTN_ERR_SHAPE;
+  if ((int64_t)used * B * H * Nq * d > ((int64_t)1 << 40)) return ATTN_ERR_SHAPE;
+  if (used > 0 && (!o_part || !lse_part)) return ATTN_ERR_NULL;
+  if (!aligned16(o_part) || !aligned16(lse_part)) return ATTN_ERR_ALIGN;
+  if ((st = check_device()) != ATTN_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (used <= 1)  // nothing to split (or no key at all)
+    return dispatch<true>(q, k, v, o, lse, B * H, Nq, Nk, d, causal, scale, s);
+  const float c = scale * kLog2e;
+  const int off = causal ? Nk - Nq : 0;
+  const int BH = B * H;
+  if (d == 64) {
+    return causal ? launch_split<64, true>(q, k, v, o, lse, BH, Nq, Nk, off, c, used, chunk, o_part, lse_part, s)
+                  : launch_split<64, false>(q, k, v, o, lse, BH, Nq, Nk, off, c, used, chunk, o_part, lse_part, s);
+  }
+  return causal ? launch_split<128, true>(q, k, v, o, lse, BH, Nq, Nk, off, c, used, chunk, o_part, lse_part, s)
+                : launch_split<128, false>(q, k, v, o, lse, BH, Nq, Nk, off, c, used, chunk, o_part, lse_part, s);
+}
+
 extern "C" const char* attn_fwd_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
@@ -641,4 +755,4 @@ extern "C" const char* attn_fwd_strerror(int status) {
   }
 }
 
-extern "C" int attn_fwd_abi_version(void) { return 2; }
+extern "C" int attn_fwd_abi_version(void) { return 3; }

@@ -8,6 +8,12 @@ resident in HBM.  Prints ONE JSON line on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd]
 
+With ``--pass decode`` a step is one split-KV forward (attn_fwd_splitkv) of
+one query per head against a long key sequence (``--decode-b/-h/-nk``, d from
+the workload; inputs from torch's seeded CUDA generator), which is bound by
+HBM: the record gives GB/s of algorithmic traffic (Q, K, V, O, LSE) against
+the 8 TB/s peak and the time of the same call without splitting.
+
 With ``--pass bwd`` a step is one call of the backward (delta, dK/dV and dQ
 kernels) on the same workload, with dO the next draw of the input generator;
 it counts 10*B*H*N^2*d flops (the five products QK^T, dO V^T, P^T dO, dS^T Q,
@@ -148,14 +154,98 @@ def cpu_baseline_bwd(w, q, k, v, dout, threads: int):
     return rec, grads
 
 
+def bench_decode(args, w, dev) -> int:
+    """One query per head against Nk keys, split-KV forward; HBM-bound."""
+    import numpy as np
+    import torch
+    import attention_attn_fwd_08_amd as af
+    import oracle
+    B, H, Nk, d = args.decode_b, args.decode_h, args.decode_nk, w.d
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    q = torch.randn(B, H, 1, d, device=dev, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, H, Nk, d, device=dev, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, H, Nk, d, device=dev, generator=g).to(torch.bfloat16)
+    n_splits = af.splitkv_splits(B, H, 1, Nk, d)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, 1, device=dev)
+    o_part = torch.empty(n_splits, B, H, 1, d, device=dev)
+    lse_part = torch.empty(n_splits, B, H, 1, device=dev)
+    log(f"decode: B={B} H={H} Nq=1 Nk={Nk} d={d}, {n_splits} splits")
+
+    def timed(fn, steps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream(dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        t0 = time.perf_counter()
+        for s_ev, e_ev in evs:
+            s_ev.record(stream)
+            fn()
+            e_ev.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        return wall, sorted(s_ev.elapsed_time(e_ev) for s_ev, e_ev in evs)
+
+    split = lambda: af.attn_fwd_splitkv(q, k, v, scale=w.scale, n_splits=n_splits, out=o, lse=lse,  # noqa: E731
+                                        o_part=o_part, lse_part=lse_part)
+    plain = lambda: af.attn_fwd_ex(q, k, v, scale=w.scale, out=o, lse=lse)  # noqa: E731
+    wall, ts = timed(split, args.steps)
+    _, tp = timed(plain, max(3, args.steps // 5))
+    kmean = sum(ts) / len(ts)
+    nbytes = 2 * B * H * Nk * d * 2 + 2 * B * H * d * 2 + B * H * 4
+    flops = 4.0 * B * H * Nk * d
+    # parity of the timed configuration against the oracle, every head
+    to_bits = lambda t: t.float().cpu().numpy().astype(np.float32).view(np.uint32)  # noqa: E731
+    bits = [((to_bits(t) >> 16).astype(np.uint16)) for t in (q, k, v)]
+    split()
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ex(*bits, False, w.scale, threads=min(16, os.cpu_count() or 1))
+    eo = np.abs(o.float().cpu().numpy() - o_ref)
+    el = np.abs(lse.cpu().numpy() - lse_ref)
+    ok = eo.max() <= O_MAX_TOL and eo.mean() <= O_MEAN_TOL and el.max() <= LSE_MAX_TOL
+    result = {
+        "metric": "split-KV decode attention: HBM GB/s of algorithmic traffic (Nq = 1)",
+        "value": round(nbytes / (wall * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"decode-B{B}-H{H}-Nq1-Nk{Nk}-d{d}", "B": B, "H": H, "Nq": 1,
+                   "Nk": Nk, "d": d, "causal": False, "scale": w.scale, "n_splits": n_splits,
+                   "seed": w.seed, "parallelism": "none", "pass": "decode"},
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (kmean * 1e-3) / 1e9, 1),
+                     "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(nbytes / (kmean * 1e-3) / 1e9 / 8000.0, 4), "traffic": None,
+                     "kernel_avg_ms": round(kmean, 5), "bytes_per_launch": nbytes,
+                     "flop_per_launch": flops,
+                     "unit_of_launch": "split kernel and merge kernel"},
+        "timing": {"kernel_ms_mean": round(kmean, 5), "kernel_ms_median": round(ts[len(ts) // 2], 5),
+                   "kernel_ms_min": round(ts[0], 5),
+                   "unsplit_kernel_ms_median": round(tp[len(tp) // 2], 5)},
+        "cpu_baseline": None,
+        "parity": {"heads": B * H, "o_max_err": float(eo.max()), "o_mean_err": float(eo.mean()),
+                   "lse_max_err": float(el.max()), "ok": bool(ok)},
+    }
+    log(f"split {kmean:.4f} ms vs unsplit {tp[len(tp) // 2]:.4f} ms; parity {result['parity']}")
+    print(json.dumps(result), flush=True)
+    return 0 if ok else 1
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
-    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
-                    help="time the forward (default) or the backward")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "decode"],
+                    help="time the forward (default), the backward, or a split-KV decode")
+    ap.add_argument("--decode-b", type=int, default=1)
+    ap.add_argument("--decode-h", type=int, default=32)
+    ap.add_argument("--decode-nk", type=int, default=65536)
     ap.add_argument("--cpu-gflop", type=float, default=80.0,
                     help="size of the oracle sample for the CPU baseline (fp64 GFLOP)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -195,6 +285,8 @@ def main() -> int:
         log(f"copied {n} bytes 3 times")
         return 0
     w = WORKLOADS[args.workload]
+    if args.which == "decode":
+        return bench_decode(args, w, dev)
     log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
 
     t0 = time.perf_counter()

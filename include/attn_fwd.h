@@ -100,10 +100,37 @@ int attn_fwd_ex(const void *q, const void *k, const void *v,
                 int causal, float scale,
                 void *stream);
 
+/*
+ * attn_fwd_splitkv -- attn_fwd_ex computed as n_splits independent key
+ * ranges of whole 64-key tiles, processed by separate workgroups, then merged
+ * per row: lse = ln sum_s exp(lse_s) and o = sum_s exp(lse_s - lse) o_s (the
+ * result is attn_fwd_ex's up to rounding).  It fills the GPU when
+ * B*H*ceil(Nq/256) workgroups are too few, e.g. Nq = 1 against a long Nk.
+ *
+ *   n_splits  requested number of key ranges, >= 1.  Ranges are
+ *             ceil(Nk / n_splits) keys rounded up to a multiple of 64, so the
+ *             number used, n_used = ceil(Nk / range), may be smaller;
+ *             n_used <= 1 runs attn_fwd_ex directly.
+ *   o_part    caller workspace, fp32 [n_splits, B, H, Nq, d] (device, 16-byte
+ *             aligned); lse_part  fp32 [n_splits, B, H, Nq].  Only the first
+ *             n_used slices are written and read; their contents afterwards
+ *             are unspecified.  Either may be NULL when n_used <= 1.
+ *
+ * Every other argument, and ownership, errors and semantics, are as for
+ * attn_fwd_ex.  Two kernels run on `stream` (the splits, then the merge).
+ */
+int attn_fwd_splitkv(const void *q, const void *k, const void *v,
+                     void *o, float *lse,
+                     int B, int H, int Nq, int Nk, int d,
+                     int causal, float scale,
+                     int n_splits, float *o_part, float *lse_part,
+                     void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *attn_fwd_strerror(int status);
 
-/* ABI version of this header's entry points (currently 2: attn_fwd_ex added). */
+/* ABI version of this header's entry points (currently 3: attn_fwd_ex and
+ * attn_fwd_splitkv added to version 1). */
 int attn_fwd_abi_version(void);
 
 #ifdef __cplusplus

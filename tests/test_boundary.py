@@ -40,7 +40,7 @@ def declared_functions():
 def test_headers_declare_the_entry_points():
     assert [os.path.basename(h) for h in HEADERS] == ["attn_bwd.h", "attn_fwd.h"]
     assert declared_functions() == ["attn_bwd", "attn_fwd", "attn_fwd_abi_version",
-                                    "attn_fwd_ex", "attn_fwd_strerror"]
+                                    "attn_fwd_ex", "attn_fwd_splitkv", "attn_fwd_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -57,7 +57,7 @@ def test_status_codes_match_header(lib):
         msg = af.attn_fwd_strerror(value)
         assert msg and msg != "unknown status"
     assert af.attn_fwd_strerror(12345) == "unknown status"
-    assert lib.attn_fwd_abi_version() == 2
+    assert lib.attn_fwd_abi_version() == 3
 
 
 def call(B=2, H=3, N=256, d=128, causal=0, scale=0.088, q=FAKE, k=FAKE, v=FAKE, o=FAKE,
@@ -185,3 +185,36 @@ def test_ex_rejects(lib, kw, status):
 @pytest.mark.parametrize("kw", [dict(Nq=0), dict(B=0), dict(Nq=0, q=0, k=0, v=0, o=0, lse=0)])
 def test_ex_empty_problem_is_a_noop(lib, kw):
     assert call_ex(**kw) == af.Status.OK
+
+
+def call_split(B=2, H=3, Nq=1, Nk=4096, d=128, causal=0, scale=0.088, n_splits=16, q=FAKE, k=FAKE,
+               v=FAKE, o=FAKE, lse=FAKE, o_part=FAKE, lse_part=FAKE):
+    return af.attn_fwd_splitkv_raw(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, n_splits,
+                                   o_part, lse_part)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_splits=0), af.Status.ERR_SHAPE),
+    (dict(n_splits=-3), af.Status.ERR_SHAPE),
+    (dict(Nk=-1), af.Status.ERR_SHAPE),
+    (dict(d=32), af.Status.ERR_HEAD_DIM),
+    (dict(o_part=0), af.Status.ERR_NULL),
+    (dict(lse_part=0), af.Status.ERR_NULL),
+    (dict(q=0), af.Status.ERR_NULL),
+    (dict(o_part=FAKE + 4), af.Status.ERR_ALIGN),
+    (dict(lse_part=FAKE + 8), af.Status.ERR_ALIGN),
+    (dict(Nk=1 << 22, n_splits=1 << 16), af.Status.ERR_SHAPE),
+])
+def test_splitkv_rejects(lib, kw, status):
+    assert call_split(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(Nq=0), dict(H=0), dict(Nq=0, o_part=0, lse_part=0)])
+def test_splitkv_empty_problem_is_a_noop(lib, kw):
+    assert call_split(**kw) == af.Status.OK
+
+
+def test_splitkv_split_choice():
+    assert af.splitkv_splits(1, 8, 1, 65536, 128) == 64
+    assert af.splitkv_splits(16, 16, 4096, 4096, 128) == 1
+    assert af.splitkv_splits(1, 1, 1, 100, 64) == 1
