@@ -64,15 +64,17 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kWave = 64;
 constexpr int kQueriesPerWave = 32;
 // Waves per workgroup: d=128 runs one 8-wave workgroup per CU (two waves per
-// SIMD; each K/V tile is fetched into LDS once per 256 queries); d=64 runs
-// 4-wave workgroups, three per CU (its register need allows three waves per
-// SIMD).
+// SIMD; each K/V tile is fetched into LDS once per 256 queries); d=32, 64 and
+// 96 run 4-wave workgroups, two or more per CU; d=256 runs one 4-wave
+// workgroup per CU, one wave per SIMD with the whole register file (its O
+// accumulator alone is 128 registers per lane).
 template <int D>
 struct Launch {
+  static_assert(D == 32 || D == 64 || D == 96 || D == 128 || D == 256, "unsupported head dim");
   static constexpr int kWaves = D == 128 ? 8 : 4;
   static constexpr int kThreads = kWave * kWaves;
   static constexpr int kBlockM = kWaves * kQueriesPerWave;  // queries per workgroup
-  static constexpr int kMinBlocks = D == 128 ? 1 : 2;      // launch-bounds occupancy hint
+  static constexpr int kMinBlocks = (D == 128 || D == 256) ? 1 : 2;  // launch-bounds occupancy hint
 };
 constexpr int kBlockN = 64;                        // keys per LDS stage
 constexpr int kXcds = 8;
@@ -91,23 +93,40 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // the 8-byte transposed reads 32 lanes at a time, 256 bytes per pass).
 //
 // K is read as the MFMA A operand: 16 lanes read the same chunk of 16
-// consecutive rows.  d=128: XOR with row%16 puts them in 16 distinct chunk
-// positions.  d=64 (128-byte rows, two rows per 256-byte pass): the 8 even
-// and the 8 odd rows of the 16 each land in distinct chunks.
+// consecutive rows.  d=128 and d=256 (rows a multiple of 256 bytes): XOR with
+// row%16 puts them in 16 distinct chunk positions.  d=64 (128-byte rows, two
+// rows per 256-byte pass): the 8 even and the 8 odd rows of the 16 each land
+// in distinct chunks.  d=32 and d=96 (row stride 4 or 12 chunks, so rows
+// r, r+4, r+8, r+12 share a bank group and the four residues of r mod 4 use
+// disjoint ones): XOR with (row/4)%4 separates the four rows of a residue
+// inside their group of four chunks (and keeps a chunk below D/8).
 //
 // V is read with ds_read_b64_tr_b16: 32 lanes read 4 consecutive rows x 2
 // adjacent 32-byte chunk pairs; the XOR moves the pair index by 2*(row%4) (+1
 // every 4 rows), so the 8 (row, pair) reads cover 8 distinct pair positions.
 // d=64: the two even (and two odd) rows of the 4 get pair offsets 0 and 2.
+// d=32 (the 4 rows are 256 contiguous bytes) and d=96 (row offsets 0, 192,
+// 384, 576 fall in 4 distinct 64-byte bank quarters) need no swizzle.
 template <int D>
 __device__ __forceinline__ int k_swz(int row) {
-  if constexpr (D == 128) return row & 15;
-  else return (row & 7) ^ ((row >> 3) & 1);
+  if constexpr (D == 128 || D == 256) return row & 15;
+  else if constexpr (D == 64) return (row & 7) ^ ((row >> 3) & 1);
+  else return (row >> 2) & 3;
 }
 template <int D>
 __device__ __forceinline__ int v_swz(int row) {
-  if constexpr (D == 128) return 4 * (row & 3) + 2 * ((row >> 2) & 1);
-  else return 4 * ((row >> 1) & 1);
+  if constexpr (D == 128 || D == 256) return 4 * (row & 3) + 2 * ((row >> 2) & 1);
+  else if constexpr (D == 64) return 4 * ((row >> 1) & 1);
+  else return 0;
+}
+// Byte offset of 32-feature block b of a V row read at `off` (block 0): with
+// rows a multiple of 128 bytes the block index is chunk bits 2.. of the
+// swizzled offset (XOR, which composes with the swizzle); d=96 rows are not,
+// and are unswizzled, so the block is a plain displacement.
+template <int D>
+__device__ __forceinline__ int v_block(int off, int b) {
+  if constexpr (D == 96) return off + 64 * b;
+  else return off ^ (b << 6);
 }
 
 // 16 bytes global -> LDS without passing through registers, through a buffer
@@ -247,10 +266,11 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   constexpr int kSteps = T::kSteps;
   constexpr int kDBlocks = T::kDBlocks;
   constexpr int kStageBytes = T::kStageBytes;
-  constexpr int kRowsPerLoad = kWave * 16 / kRowBytes;              // rows one wave load fills
   constexpr int kWaves = Launch<D>::kWaves;
   constexpr int kBlockM = Launch<D>::kBlockM;
-  constexpr int kLoadsPerWave = kBlockN / (kRowsPerLoad * kWaves);  // per tensor per stage
+  constexpr int kLoadBytes = kWave * 16;                              // one wave load
+  constexpr int kLoadsPerWave = kStageBytes / (kLoadBytes * kWaves);  // per tensor per stage
+  static_assert(kStageBytes % (kLoadBytes * kWaves) == 0, "stage must split evenly over the waves");
 
   // K stages 0,1 then V stages 0,1.
   __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * kStageBytes];
@@ -326,28 +346,29 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
   }
 
-  // Global -> LDS copy of one K or V tile.  Lane i of a wave load fills
-  // bytes [16i, 16i+16) after the wave's base: row base+i/kChunksPerRow,
-  // physical chunk i%kChunksPerRow, which holds logical chunk (that ^ swz).
-  // The buffer starts at the tile, so rows past N fall outside its size.
-  const int ld_row = lane / kChunksPerRow;
-  const int ld_chunk = lane % kChunksPerRow;
+  // Global -> LDS copy of one K or V tile.  The stage is a row-major array of
+  // 16-byte chunks; lane i of wave load w fills chunk g = 64w + i (bytes
+  // [16g, 16g+16)): row g/kChunksPerRow, physical chunk g%kChunksPerRow,
+  // which holds logical chunk (that ^ swz).  The buffer starts at the tile,
+  // so rows past the keys fall outside its size.
   int k_ld_off[kLoadsPerWave], v_ld_off[kLoadsPerWave];
 #pragma unroll
   for (int it = 0; it < kLoadsPerWave; ++it) {
-    const int row = (wave * kLoadsPerWave + it) * kRowsPerLoad + ld_row;
-    k_ld_off[it] = row * kRowBytes + ((ld_chunk ^ k_swz<D>(row)) << 4);
-    v_ld_off[it] = row * kRowBytes + ((ld_chunk ^ v_swz<D>(row)) << 4);
+    const unsigned g = (wave * kLoadsPerWave + it) * kWave + lane;
+    const int row = (int)(g / kChunksPerRow);
+    const int chunk = (int)(g % kChunksPerRow);
+    k_ld_off[it] = row * kRowBytes + ((chunk ^ k_swz<D>(row)) << 4);
+    v_ld_off[it] = row * kRowBytes + ((chunk ^ v_swz<D>(row)) << 4);
   }
   const unsigned lds_wave = (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)smem +
-                            wave * kLoadsPerWave * kRowsPerLoad * kRowBytes;
+                            wave * kLoadsPerWave * kLoadBytes;
   auto load_tile = [&](const __bf16* base, const int (&ld_off)[kLoadsPerWave], int region,
                        int tile, int stage) __attribute__((always_inline)) {
     const i32x4 rsrc = make_rsrc(base + (size_t)tile * kBlockN * D, (Nk - tile * kBlockN) * kRowBytes);
     const unsigned dst = lds_wave + (2 * region + stage) * kStageBytes;
 #pragma unroll
     for (int it = 0; it < kLoadsPerWave; ++it)
-      load16_to_lds(rsrc, ld_off[it], dst + it * kRowsPerLoad * kRowBytes);
+      load16_to_lds(rsrc, ld_off[it], dst + it * kLoadBytes);
   };
   auto load_k = [&](int tile, int stage) __attribute__((always_inline)) {
     load_tile(kh, k_ld_off, 0, tile, stage);
@@ -401,6 +422,21 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
   wait_lds_dma<0>();
   __syncthreads();  // K0, V0, K1 have landed
+
+  if constexpr (GENERAL) {
+    // A wave whose 32 queries all lie past the last query (a short query
+    // block, e.g. decoding) computes nothing; it still issues its share of
+    // the copies and meets every barrier the tile loop below does.
+    if (q0 >= N) {
+      for (int t = 0; t < n_tiles; ++t) {
+        wait_lds_dma<0>();
+        __syncthreads();
+        if (t + 2 < n_tiles) load_k(t + 2, t & 1);
+        if (t + 1 < n_tiles) load_v(t + 1, (t + 1) & 1);
+      }
+      return;
+    }
+  }
 
   // Prologue: scores of tile 0 and the first reference maximum.  Tile 0
   // holds key 0, which every query sees, so the maximum is finite.
@@ -476,8 +512,8 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
           const unsigned char* a = v_lds + (sb * 32 + cc * 16) * kRowBytes;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + (v_off[0] ^ (b << 6))));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + (v_off[1] ^ (b << 6))));
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + v_block<D>(v_off[0], b)));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + v_block<D>(v_off[1], b)));
           const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[sb][cc], acc[b], 0, 0, 0);
         }
@@ -567,7 +603,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
                                                          float* __restrict__ lse, long long rows,
                                                          int n_splits) {
   constexpr int kPerRow = D / 4;
-  const long long row = (long long)blockIdx.x * (256 / kPerRow) + threadIdx.x / kPerRow;
+  constexpr int kRowsPerBlock = 256 / kPerRow;
+  if (threadIdx.x >= kRowsPerBlock * kPerRow) return;  // d=96: 240 of the 256 threads
+  const long long row = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / kPerRow;
   const int f = (threadIdx.x % kPerRow) * 4;
   if (row >= rows) return;
   float m = -INFINITY;
@@ -648,20 +686,28 @@ int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, i
              int Nk, int d, int causal, float scale, hipStream_t s) {
   const float c = scale * kLog2e;
   const int off = causal ? Nk - Nq : 0;
-  if (d == 64) {
-    return causal ? launch<64, true, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, s)
-                  : launch<64, false, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, s);
+  auto go = [&](auto d_tag) {
+    constexpr int D = decltype(d_tag)::value;
+    return causal ? launch<D, true, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, s)
+                  : launch<D, false, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, s);
+  };
+  switch (d) {
+    case 32: return go(std::integral_constant<int, 32>{});
+    case 64: return go(std::integral_constant<int, 64>{});
+    case 96: return go(std::integral_constant<int, 96>{});
+    case 128: return go(std::integral_constant<int, 128>{});
+    default: return go(std::integral_constant<int, 256>{});
   }
-  return causal ? launch<128, true, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, s)
-                : launch<128, false, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, s);
 }
+
+bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 96 || d == 128 || d == 256; }
 
 // Argument checks shared by the entry points (before any HIP call).
 int check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
                int B, int H, int Nq, int Nk, int d, float scale, bool* nothing) {
   *nothing = false;
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (!head_dim_ok(d)) return ATTN_ERR_HEAD_DIM;
   if (!(scale > 0.0f) || !isfinite(scale)) return ATTN_ERR_SCALE;
   const int64_t bh = (int64_t)B * H;
   if (bh > INT32_MAX) return ATTN_ERR_SHAPE;
@@ -732,12 +778,19 @@ extern "C" int attn_fwd_splitkv(const void* q, const void* k, const void* v, voi
   const float c = scale * kLog2e;
   const int off = causal ? Nk - Nq : 0;
   const int BH = B * H;
-  if (d == 64) {
-    return causal ? launch_split<64, true>(q, k, v, o, lse, BH, Nq, Nk, off, c, used, chunk, o_part, lse_part, s)
-                  : launch_split<64, false>(q, k, v, o, lse, BH, Nq, Nk, off, c, used, chunk, o_part, lse_part, s);
+  auto go = [&](auto d_tag) {
+    constexpr int D = decltype(d_tag)::value;
+    return causal
+               ? launch_split<D, true>(q, k, v, o, lse, BH, Nq, Nk, off, c, used, chunk, o_part, lse_part, s)
+               : launch_split<D, false>(q, k, v, o, lse, BH, Nq, Nk, off, c, used, chunk, o_part, lse_part, s);
+  };
+  switch (d) {
+    case 32: return go(std::integral_constant<int, 32>{});
+    case 64: return go(std::integral_constant<int, 64>{});
+    case 96: return go(std::integral_constant<int, 96>{});
+    case 128: return go(std::integral_constant<int, 128>{});
+    default: return go(std::integral_constant<int, 256>{});
   }
-  return causal ? launch_split<128, true>(q, k, v, o, lse, BH, Nq, Nk, off, c, used, chunk, o_part, lse_part, s)
-                : launch_split<128, false>(q, k, v, o, lse, BH, Nq, Nk, off, c, used, chunk, o_part, lse_part, s);
 }
 
 extern "C" const char* attn_fwd_strerror(int status) {
@@ -745,7 +798,7 @@ extern "C" const char* attn_fwd_strerror(int status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "B, H or N is negative, or the problem size overflows";
-    case ATTN_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
+    case ATTN_ERR_HEAD_DIM: return "head dimension d must be 32, 64, 96, 128 or 256 (backward: 64 or 128)";
     case ATTN_ERR_SEQ_MULTIPLE: return "reserved (any sequence length is accepted)";
     case ATTN_ERR_ALIGN: return "q, k, v, o and lse must be 16-byte aligned";
     case ATTN_ERR_SCALE: return "scale must be finite and greater than 0";

@@ -36,7 +36,7 @@ enum attn_fwd_status {
     ATTN_OK = 0,               /* launched (or nothing to do)                  */
     ATTN_ERR_NULL = 1,         /* a pointer is NULL while B*H*N > 0            */
     ATTN_ERR_SHAPE = 2,        /* B, H or N negative, or the sizes overflow    */
-    ATTN_ERR_HEAD_DIM = 3,     /* d is not 64 or 128                           */
+    ATTN_ERR_HEAD_DIM = 3,     /* d not in {32, 64, 96, 128, 256} (forward)   */
     ATTN_ERR_SEQ_MULTIPLE = 4, /* reserved: any N >= 0 is accepted             */
     ATTN_ERR_ALIGN = 5,        /* a pointer is not 16-byte aligned             */
     ATTN_ERR_SCALE = 6,        /* scale is not finite or not > 0               */
@@ -56,8 +56,11 @@ enum attn_fwd_status {
  *            scaled scores.  Required (not optional).
  *   B, H, N  batch, heads, sequence length (queries = keys = N).  Any of them
  *            may be 0 (nothing is launched); N need not be a multiple of any
- *            tile size.  B*H*ceil(N/256) and N*d*2 must fit in an int.
- *   d        head dimension: 64 or 128.
+ *            tile size.  B*H*ceil(N/128) and N*d*2 must fit in an int.
+ *   d        head dimension: 32, 64, 96, 128 or 256.  (The examples fix d:
+ *            64 on the RTX 4090, 64 or 128 as a template parameter on the
+ *            H100; the other sizes are this library's extension, computed
+ *            with the same 16-deep MFMA steps and 32-wide output blocks.)
  *   causal   0: every query sees every key.  Non-zero: query i sees keys
  *            0..i (lower-triangular mask, top-left aligned).
  *   scale    multiplies q.k; finite and > 0 (1/sqrt(d) is the usual value).

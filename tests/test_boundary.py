@@ -69,8 +69,9 @@ def call(B=2, H=3, N=256, d=128, causal=0, scale=0.088, q=FAKE, k=FAKE, v=FAKE, 
     (dict(B=-1), af.Status.ERR_SHAPE),
     (dict(H=-2), af.Status.ERR_SHAPE),
     (dict(N=-128), af.Status.ERR_SHAPE),
-    (dict(d=32), af.Status.ERR_HEAD_DIM),
-    (dict(d=96), af.Status.ERR_HEAD_DIM),
+    (dict(d=16), af.Status.ERR_HEAD_DIM),
+    (dict(d=48), af.Status.ERR_HEAD_DIM),
+    (dict(d=512), af.Status.ERR_HEAD_DIM),
     (dict(d=0), af.Status.ERR_HEAD_DIM),
     (dict(scale=0.0), af.Status.ERR_SCALE),
     (dict(scale=-0.1), af.Status.ERR_SCALE),
@@ -100,6 +101,17 @@ def test_rejects(lib, kw, status):
                                 dict(B=0, q=0, k=0, v=0, o=0, lse=0)])
 def test_empty_problem_is_a_noop(lib, kw):
     assert call(**kw) == af.Status.OK
+
+
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
+def test_forward_head_dims_pass_the_argument_checks(lib, d):
+    """Every supported d gets past the argument checks of the three forward
+    entry points (an empty problem returns OK before any device call; the
+    same arguments with a head dim off the list do not)."""
+    assert call(d=d, B=0) == af.Status.OK
+    assert call_ex(d=d, Nq=0) == af.Status.OK
+    assert call_split(d=d, Nq=0) == af.Status.OK
+    assert call(d=d + 8, B=0) == af.Status.ERR_HEAD_DIM
 
 
 def test_python_binding_rejects_cpu_tensors():
@@ -168,7 +180,7 @@ def call_ex(B=2, H=3, Nq=100, Nk=300, d=128, causal=1, scale=0.088, q=FAKE, k=FA
 @pytest.mark.parametrize("kw,status", [
     (dict(Nq=-1), af.Status.ERR_SHAPE),
     (dict(Nk=-1), af.Status.ERR_SHAPE),
-    (dict(d=96), af.Status.ERR_HEAD_DIM),
+    (dict(d=80), af.Status.ERR_HEAD_DIM),
     (dict(scale=-1.0), af.Status.ERR_SCALE),
     (dict(Nk=1 << 24), af.Status.ERR_SHAPE),
     (dict(Nq=1 << 24), af.Status.ERR_SHAPE),
@@ -197,7 +209,7 @@ def call_split(B=2, H=3, Nq=1, Nk=4096, d=128, causal=0, scale=0.088, n_splits=1
     (dict(n_splits=0), af.Status.ERR_SHAPE),
     (dict(n_splits=-3), af.Status.ERR_SHAPE),
     (dict(Nk=-1), af.Status.ERR_SHAPE),
-    (dict(d=32), af.Status.ERR_HEAD_DIM),
+    (dict(d=160), af.Status.ERR_HEAD_DIM),
     (dict(o_part=0), af.Status.ERR_NULL),
     (dict(lse_part=0), af.Status.ERR_NULL),
     (dict(q=0), af.Status.ERR_NULL),

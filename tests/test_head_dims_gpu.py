@@ -1,0 +1,75 @@
+"""GPU parity at the head dims beyond 64 and 128 (32, 96 and 256) against the
+fp64 oracles, for the three forward entry points, at the forward's
+tolerances: several query and key tiles, ragged tails, causal and not, and a
+sharp-score case (q, k with sigma 2) that exercises the rescale path."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from attention_attn_fwd_08_amd.inputs import f32_to_bf16_bits, make_qkv
+from gpu_util import (LSE_MAX_TOL, O_MAX_TOL, O_MEAN_TOL, ORACLE_THREADS, assert_parity, log, run_gpu,
+                      to_device, to_host_f64)
+
+pytestmark = pytest.mark.gpu
+
+SQUARE = [
+    # B, H, N, d, causal, qk_sigma
+    (2, 2, 384, 32, False, 1.0), (2, 2, 384, 32, True, 2.0), (1, 3, 1000, 32, True, 1.0),
+    (2, 2, 384, 96, False, 1.0), (2, 2, 384, 96, True, 2.0), (1, 3, 1000, 96, False, 1.0),
+    (2, 2, 384, 256, False, 1.0), (2, 2, 384, 256, True, 2.0), (1, 3, 1000, 256, True, 1.0),
+    (1, 1, 1, 96, False, 1.0), (1, 2, 33, 256, False, 1.0), (2, 1, 77, 32, True, 1.0),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,sigma", SQUARE)
+def test_square_full(B, H, N, d, causal, sigma):
+    log(f"[head dim] B={B} H={H} N={N} d={d} causal={causal} sigma={sigma}")
+    q, k, v = make_qkv(B, H, N, d, seed=300 + N + d, qk_sigma=sigma)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run_gpu(q, k, v, causal, scale)
+    o_ref, lse_ref = oracle.attention(q, k, v, causal, scale, threads=ORACLE_THREADS)
+    assert_parity(to_host_f64(o), to_host_f64(lse), o_ref, lse_ref, f"d={d}")
+
+
+def _bits(rng, shape):
+    return f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
+
+
+def _check_general(o, lse, o_ref, lse_ref):
+    o_g, l_g = to_host_f64(o), lse.cpu().numpy().astype(np.float64)
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(l_g), empty), "rows without keys must have lse = -inf"
+    assert np.all(o_g[empty] == 0.0), "rows without keys must have o = 0"
+    full = ~empty
+    eo = np.abs(o_g[full] - o_ref[full])
+    el = np.abs(l_g[full] - lse_ref[full])
+    log(f"  O max {eo.max():.3e} mean {eo.mean():.3e}  LSE max {el.max():.3e}")
+    assert eo.max() <= O_MAX_TOL and eo.mean() <= O_MEAN_TOL and el.max() <= LSE_MAX_TOL
+
+
+GENERAL = [
+    # B, H, Nq, Nk, d, causal, n_splits (1: attn_fwd_ex; > 1: attn_fwd_splitkv)
+    (1, 2, 100, 300, 32, True, 1), (1, 2, 300, 100, 96, True, 1), (1, 2, 70, 500, 256, False, 1),
+    (1, 4, 1, 3000, 32, False, 8), (1, 4, 1, 3000, 96, True, 8), (1, 4, 5, 3000, 256, True, 8),
+    (1, 2, 200, 900, 96, False, 3), (1, 2, 300, 200, 256, True, 2),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal,n_splits", GENERAL)
+def test_general_shapes(B, H, Nq, Nk, d, causal, n_splits):
+    import torch
+    import attention_attn_fwd_08_amd as af
+    log(f"[head dim general] B{B} H{H} Nq{Nq} Nk{Nk} d{d} causal={causal} splits={n_splits}")
+    rng = np.random.default_rng(4000 + Nq + 5 * Nk + d)
+    qb, kb, vb = _bits(rng, (B, H, Nq, d)), _bits(rng, (B, H, Nk, d)), _bits(rng, (B, H, Nk, d))
+    scale = 1.0 / np.sqrt(d)
+    q, k, v = to_device(qb), to_device(kb), to_device(vb)
+    if n_splits == 1:
+        o, lse = af.attn_fwd_ex(q, k, v, causal=causal, scale=scale)
+    else:
+        o, lse = af.attn_fwd_splitkv(q, k, v, causal=causal, scale=scale, n_splits=n_splits)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ex(qb, kb, vb, causal, scale, threads=ORACLE_THREADS)
+    _check_general(o, lse, o_ref, lse_ref)
