@@ -42,7 +42,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from attention_attn_fwd_08_amd.inputs import (HEADLINE, WORKLOADS, make_qkv_dout, sample_rows,  # noqa: E402
+from attention_attn_fwd_08_amd.inputs import (HEADLINE, WORKLOADS, Workload, make_qkv_dout, sample_rows,  # noqa: E402
                                               workload_inputs)
 
 # MI355X published dense bf16 MFMA peak: 256 CUs x 4096 flop/clk/CU x 2.4 GHz.
@@ -241,6 +241,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--shape", default=None, metavar="B,H,N,d[,causal]",
+                    help="time this problem instead of a named workload (seed 0, sigma 1)")
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "decode"],
                     help="time the forward (default), the backward, or a split-KV decode")
     ap.add_argument("--decode-b", type=int, default=1)
@@ -285,6 +287,14 @@ def main() -> int:
         log(f"copied {n} bytes 3 times")
         return 0
     w = WORKLOADS[args.workload]
+    if args.shape:
+        f = [int(x) for x in args.shape.split(",")]
+        if len(f) not in (4, 5) or min(f[:4]) < 1:
+            print("--shape takes B,H,N,d or B,H,N,d,causal", file=sys.stderr)
+            return 2
+        causal = len(f) == 5 and f[4] != 0
+        w = Workload(f"B{f[0]}-H{f[1]}-N{f[2]}-d{f[3]}" + ("-causal" if causal else ""),
+                     f[0], f[1], f[2], f[3], causal, seed=0)
     if args.which == "decode":
         return bench_decode(args, w, dev)
     log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
