@@ -4,9 +4,10 @@ TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.  Only ``tests/``,
 ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
 this package.  It shares no code with the HIP library and never imports it.
 
-The arithmetic lives in ``attn_oracle.c`` (forward) and ``attn_bwd_oracle.c``
-(backward: the derivative of the same definition, full matrices per head), both
-single-threaded C with libm exp/log in fp64.  This module only compiles that file with gcc, loads it with ctypes and
+The arithmetic lives in ``attn_oracle.c`` (forward), ``attn_bwd_oracle.c``
+(backward: the derivative of the same definition, full matrices per head) and
+``gemm_oracle.c`` (the plain matrix product), all single-threaded C, fp64,
+with libm exp/log.  This module only compiles that file with gcc, loads it with ctypes and
 hands it buffers.  ``threads > 1`` splits the list of query rows between host
 threads, each running the same single-threaded C routine on its own rows (the
 rows are independent, so the result does not depend on the split).
@@ -33,7 +34,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "attn_oracle.c")
-SOURCES = (SOURCE, os.path.join(_HERE, "attn_bwd_oracle.c"))
+SOURCES = (SOURCE, os.path.join(_HERE, "attn_bwd_oracle.c"), os.path.join(_HERE, "gemm_oracle.c"))
+GEMM_SOURCE = SOURCES[2]
 LIBRARY = os.path.join(_HERE, "libattn_oracle.so")
 
 _lock = threading.Lock()
@@ -61,10 +63,11 @@ def build(sources=SOURCES, output: str = LIBRARY) -> str:
 
 def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     i64, u16p, f64p = ctypes.c_int64, ctypes.POINTER(ctypes.c_uint16), ctypes.POINTER(ctypes.c_double)
-    lib.attn_oracle_rows.argtypes = [
-        u16p, u16p, u16p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double,
-        ctypes.POINTER(ctypes.c_int64), i64, f64p, f64p]
-    lib.attn_oracle_rows.restype = ctypes.c_int
+    if hasattr(lib, "attn_oracle_rows"):
+        lib.attn_oracle_rows.argtypes = [
+            u16p, u16p, u16p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double,
+            ctypes.POINTER(ctypes.c_int64), i64, f64p, f64p]
+        lib.attn_oracle_rows.restype = ctypes.c_int
     if hasattr(lib, "attn_oracle_rows_ex"):
         lib.attn_oracle_rows_ex.argtypes = [
             u16p, u16p, u16p, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double,
@@ -82,6 +85,10 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
             f64p, f64p, f64p, f64p, i64, i64, ctypes.c_int, ctypes.c_double,
             f64p, f64p, f64p, f64p, f64p, f64p, f64p]
         lib.attn_bwd_oracle_head_f64.restype = ctypes.c_int
+    if hasattr(lib, "gemm_oracle_rows"):
+        lib.gemm_oracle_rows.argtypes = [u16p, u16p, i64, i64, i64, ctypes.c_int,
+                                         ctypes.POINTER(ctypes.c_int64), i64, f64p]
+        lib.gemm_oracle_rows.restype = ctypes.c_int
     return lib
 
 
@@ -285,3 +292,53 @@ def attention_ex(q, k, v, causal: bool, scale: float, threads: int = 1,
     if any(s != 0 for s in statuses):
         raise RuntimeError(f"oracle failed with status {statuses}")
     return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
+
+
+# ---------------------------------------------------------------------------
+# Matrix product (gemm_oracle.c)
+# ---------------------------------------------------------------------------
+
+def gemm(a, b, b_layout: str = "nn", rows=None, threads: int = 1, lib: ctypes.CDLL | None = None):
+    """C = A B (``b_layout="nn"``, b is [K, N]) or C = A B^T (``"nt"``, b is
+    [N, K]) for bf16-bit a [M, K], in fp64.  ``rows``: the rows of C to
+    compute (default all); returns float64 [len(rows), N].  ``threads > 1``
+    splits the rows between host threads."""
+    for name, x in (("a", a), ("b", b)):
+        if not isinstance(x, np.ndarray) or x.dtype != np.uint16 or x.ndim != 2:
+            raise TypeError(f"{name} must be a 2-D numpy uint16 array of bf16 bits")
+    if b_layout not in ("nn", "nt"):
+        raise ValueError("b_layout must be 'nn' or 'nt'")
+    a, b = np.ascontiguousarray(a), np.ascontiguousarray(b)
+    M, K = a.shape
+    if b_layout == "nn":
+        if b.shape[0] != K:
+            raise ValueError("b must be [K, N]")
+        N = b.shape[1]
+    else:
+        if b.shape[1] != K:
+            raise ValueError("b must be [N, K]")
+        N = b.shape[0]
+    rows = np.arange(M, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64).reshape(-1)
+    rows = np.ascontiguousarray(rows)
+    lib = lib or load()
+    c = np.zeros((rows.size, N))
+    threads = max(1, min(int(threads), rows.size or 1))
+    bounds = np.linspace(0, rows.size, threads + 1).astype(np.int64)
+    lay = 0 if b_layout == "nn" else 1
+
+    def run(part):
+        lo, hi = int(bounds[part]), int(bounds[part + 1])
+        if hi <= lo:
+            return 0
+        return lib.gemm_oracle_rows(_ptr(a, ctypes.c_uint16), _ptr(b, ctypes.c_uint16), M, N, K, lay,
+                                    _ptr(rows[lo:hi], ctypes.c_int64), hi - lo,
+                                    _ptr(c[lo:hi], ctypes.c_double))
+
+    if threads == 1:
+        statuses = [run(0)]
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as pool:
+            statuses = list(pool.map(run, range(threads)))
+    if any(s != 0 for s in statuses):
+        raise RuntimeError(f"oracle failed with status {statuses}")
+    return c
