@@ -1,7 +1,7 @@
 """MI355X-native fused attention: thin Python binding over the C ABI.
 
 Every step of the computation runs in the HIP library ``libattn_fwd.so``
-(built from ``csrc/attn_fwd.hip`` and ``csrc/attn_bwd.hip`` for gfx950).  This module only checks and
+(built from ``csrc/attn_fwd.hip``, ``csrc/attn_bwd.hip`` and ``csrc/gemm.hip`` for gfx950).  This module only checks and
 marshals arguments: PyTorch supplies device memory and the current stream.
 There is no fallback: if the library is missing, calls raise.
 
@@ -14,7 +14,11 @@ ThunderKittens write-up, 88811315.cn, "H100 FlashAttention-2 forward example"), 
     dq, dk, dv, delta = attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None)
 
 its derivative for a loss whose gradient with respect to o is ``dout``
-(``delta`` = rowsum(dout * o), the backward's per-row intermediate).
+(``delta`` = rowsum(dout * o), the backward's per-row intermediate), and
+
+    c = gemm(a, b, layout="nn")
+
+the bf16 matrix product c = a b (``"nt"``: c = a b^T) on the matrix cores.
 """
 from __future__ import annotations
 
@@ -25,7 +29,8 @@ import threading
 
 __all__ = ["attn_fwd", "attn_fwd_raw", "attn_fwd_ex", "attn_fwd_ex_raw", "attn_fwd_splitkv",
            "attn_fwd_splitkv_raw", "splitkv_splits", "attn_bwd",
-           "attn_bwd_raw", "attn_fwd_strerror", "load_library", "LIBRARY", "Status", "AttnError"]
+           "attn_bwd_raw", "gemm", "gemm_raw", "GEMM_NN", "GEMM_NT", "attn_fwd_strerror",
+           "load_library", "LIBRARY", "Status", "AttnError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_HERE, "libattn_fwd.so")
@@ -86,6 +91,8 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.attn_fwd_splitkv.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [vp] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float, vp]
     lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_gemm_bf16.argtypes = [vp] * 3 + [ctypes.c_int] * 4 + [vp]
+    lib.attn_gemm_bf16.restype = ctypes.c_int
     return lib
 
 
@@ -318,3 +325,53 @@ def attn_fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
     if status != Status.OK:
         raise AttnError(status, attn_fwd_strerror(status))
     return out, lse
+
+
+# Layout codes of include/attn_gemm.h.
+GEMM_NN = 0  # b is [K, N]: c = a b
+GEMM_NT = 1  # b is [N, K]: c = a b^T
+
+
+def gemm_raw(a_ptr: int, b_ptr: int, c_ptr: int, M: int, N: int, K: int, layout: int,
+             stream: int = 0) -> int:
+    """Call ``attn_gemm_bf16`` with raw integer addresses; returns the status."""
+    lib = load_library()
+    return lib.attn_gemm_bf16(a_ptr or None, b_ptr or None, c_ptr or None, int(M), int(N), int(K),
+                              int(layout), stream or None)
+
+
+def gemm(a, b, layout: str = "nn", out=None):
+    """c = a b (``layout="nn"``, b [K, N]) or c = a b^T (``"nt"``, b [N, K])
+    for contiguous bf16 GPU matrices a [M, K]; returns c, bf16 [M, N]."""
+    import torch
+
+    for name, t in (("a", a), ("b", b)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be a bfloat16 torch.Tensor")
+        if t.device.type != "cuda" or t.dim() != 2 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 2-D GPU tensor")
+    if b.device != a.device:
+        raise ValueError("a and b must be on the same device")
+    if layout not in ("nn", "nt"):
+        raise ValueError("layout must be 'nn' or 'nt'")
+    M, K = a.shape
+    if layout == "nn":
+        if b.shape[0] != K:
+            raise ValueError("b must be [K, N]")
+        N = b.shape[1]
+    else:
+        if b.shape[1] != K:
+            raise ValueError("b must be [N, K]")
+        N = b.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    elif (not isinstance(out, torch.Tensor) or out.dtype != torch.bfloat16 or out.device != a.device
+          or tuple(out.shape) != (M, N) or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous bfloat16 [M, N] tensor on a's device")
+    with torch.cuda.device(a.device):
+        stream = torch.cuda.current_stream(a.device).cuda_stream
+        status = gemm_raw(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
+                          GEMM_NN if layout == "nn" else GEMM_NT, stream)
+    if status != Status.OK:
+        raise AttnError(status, attn_fwd_strerror(status))
+    return out

@@ -8,7 +8,7 @@ import tempfile
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCE = os.path.join(PKG, "csrc", "attn_fwd.hip")
-SOURCES = (SOURCE, os.path.join(PKG, "csrc", "attn_bwd.hip"))
+SOURCES = (SOURCE, os.path.join(PKG, "csrc", "attn_bwd.hip"), os.path.join(PKG, "csrc", "gemm.hip"))
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libattn_fwd.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -14,6 +14,12 @@ the workload; inputs from torch's seeded CUDA generator), which is bound by
 HBM: the record gives GB/s of algorithmic traffic (Q, K, V, O, LSE) against
 the 8 TB/s peak and the time of the same call without splitting.
 
+With ``--pass gemm`` a step is one bf16 matrix product C = A B (``--gemm-layout
+nn``) or A B^T (``nt``) of ``--gemm-size`` M,N,K (default 8192^3) on the
+matrix cores, reported in TFLOP/s (2 M N K flop) against the bf16 MFMA peak,
+with the same product through torch.matmul (the vendor BLAS) timed beside it
+and the oracle on a sample of rows as the CPU baseline.
+
 With ``--pass bwd`` a step is one call of the backward (delta, dK/dV and dQ
 kernels) on the same workload, with dO the next draw of the input generator;
 it counts 10*B*H*N^2*d flops (the five products QK^T, dO V^T, P^T dO, dS^T Q,
@@ -235,6 +241,109 @@ def bench_decode(args, w, dev) -> int:
     return 0 if ok else 1
 
 
+def bench_gemm(args, dev) -> int:
+    """C = A B (or A B^T), bf16 in / fp32 accumulate / bf16 out, MFMA-bound."""
+    import numpy as np
+    import torch
+    import attention_attn_fwd_08_amd as af
+    import oracle
+    from attention_attn_fwd_08_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits
+    M, N, K = (int(x) for x in args.gemm_size.split(","))
+    lay = args.gemm_layout
+    rng = np.random.default_rng(8)
+    t0 = time.perf_counter()
+    a_bits = f32_to_bf16_bits(rng.standard_normal(M * K, dtype=np.float32)).reshape(M, K)
+    b_bits = f32_to_bf16_bits(rng.standard_normal(K * N, dtype=np.float32)).reshape(
+        (K, N) if lay == "nn" else (N, K))
+    log(f"gemm {M}x{N}x{K} {lay}: inputs generated in {time.perf_counter() - t0:.1f} s")
+    to_dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    a, b = to_dev(a_bits), to_dev(b_bits)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    flops = 2.0 * M * N * K
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, steps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        t_start = time.perf_counter()
+        for s_ev, e_ev in evs:
+            s_ev.record(stream)
+            fn()
+            e_ev.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t_start) * 1e3 / steps
+        return wall, sorted(s_ev.elapsed_time(e_ev) for s_ev, e_ev in evs)
+
+    ours = lambda: af.gemm(a, b, lay, out=c)  # noqa: E731
+    wall, ts = timed(ours, args.steps)
+    kmean = sum(ts) / len(ts)
+    # The vendor BLAS on the same operands (torch.matmul -> hipBLASLt), for comparison only.
+    c_ref = torch.empty_like(c)
+    bt = b if lay == "nn" else b.t()
+    vendor = lambda: torch.matmul(a, bt, out=c_ref)  # noqa: E731
+    _, tv = timed(vendor, max(5, args.steps // 2))
+    vmed = tv[len(tv) // 2]
+    ours()
+    torch.cuda.synchronize()
+    result = {
+        "metric": "bf16 GEMM TFLOP/s at 1 MI355X (2*M*N*K flop)",
+        "value": round(flops / (wall * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"gemm-{lay}-M{M}-N{N}-K{K}", "M": M, "N": N, "K": K, "layout": lay,
+                   "seed": 8, "parallelism": "none", "pass": "gemm"},
+        "roofline": {"bound": "mfma", "achieved": round(flops / (kmean * 1e-3) / 1e12, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / (kmean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel_avg_ms": round(kmean, 5), "flop_per_launch": flops,
+                     "algorithmic_hbm_bytes_per_launch": 2 * (M * K + K * N + M * N)},
+        "timing": {"kernel_ms_mean": round(kmean, 5), "kernel_ms_median": round(ts[len(ts) // 2], 5),
+                   "kernel_ms_min": round(ts[0], 5)},
+        "vendor_blas": {"library": "torch.matmul (hipBLASLt)", "kernel_ms_median": round(vmed, 5),
+                        "tflops_at_median": round(flops / (vmed * 1e-3) / 1e12, 2)},
+        "cpu_baseline": None,
+    }
+    ok = True
+    if not args.no_cpu_baseline:
+        # A first batch of rows sizes the sample to about 10 s of oracle time.
+        threads = min(16, os.cpu_count() or 1)
+        oracle.load()
+        first = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, size=2 * threads - 2)]))
+        t0 = time.perf_counter()
+        oracle.gemm(a_bits, b_bits, lay, rows=first, threads=threads)
+        per_row = (time.perf_counter() - t0) / first.size
+        n_rows = int(min(M, max(first.size, 10.0 / max(per_row, 1e-9))))
+        rows = np.unique(np.concatenate([first, rng.integers(0, M, size=n_rows)])).astype(np.int64)
+        t0 = time.perf_counter()
+        ref = oracle.gemm(a_bits, b_bits, lay, rows=rows, threads=threads)
+        dt = time.perf_counter() - t0
+        sample_flop = 2.0 * rows.size * N * K
+        result["cpu_baseline"] = {
+            "value": sample_flop / dt / 1e12, "unit": "TFLOP/s", "cores": min(threads, rows.size),
+            "kind": "oracle",
+            "sample": f"{rows.size} rows of C ({sample_flop / 1e9:.1f} GFLOP fp64) in {dt:.2f} s wall"}
+        got = bf16_bits_to_f32(c[torch.as_tensor(rows, device=dev)].view(torch.int16).cpu().numpy()
+                               .view(np.uint16)).astype(np.float64)
+        af64 = np.abs(bf16_bits_to_f32(a_bits[rows]).astype(np.float64))
+        bf64 = np.abs(bf16_bits_to_f32(b_bits).astype(np.float64))
+        mag = af64 @ (bf64 if lay == "nn" else bf64.T)
+        bound = 2.0 ** -8 * np.abs(ref) + K * 2.0 ** -22 * mag
+        err = np.abs(got - ref)
+        ok = bool(np.all(err <= bound))
+        result["parity"] = {"rows": int(rows.size), "max_abs_err": float(err.max()),
+                            "max_err_over_bound": float((err / bound).max()), "ok": ok}
+    log(f"gemm {kmean:.4f} ms ({result['roofline']['achieved']} TFLOP/s) vs vendor {vmed:.4f} ms "
+        f"({result['vendor_blas']['tflops_at_median']} TFLOP/s)")
+    print(json.dumps(result), flush=True)
+    return 0 if ok else 1
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,8 +352,10 @@ def main() -> int:
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--shape", default=None, metavar="B,H,N,d[,causal]",
                     help="time this problem instead of a named workload (seed 0, sigma 1)")
-    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "decode"],
-                    help="time the forward (default), the backward, or a split-KV decode")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "decode", "gemm"],
+                    help="time the forward (default), the backward, a split-KV decode or a GEMM")
+    ap.add_argument("--gemm-size", default="8192,8192,8192", metavar="M,N,K")
+    ap.add_argument("--gemm-layout", default="nn", choices=["nn", "nt"])
     ap.add_argument("--decode-b", type=int, default=1)
     ap.add_argument("--decode-h", type=int, default=32)
     ap.add_argument("--decode-nk", type=int, default=65536)
@@ -297,6 +408,8 @@ def main() -> int:
                      f[0], f[1], f[2], f[3], causal, seed=0)
     if args.which == "decode":
         return bench_decode(args, w, dev)
+    if args.which == "gemm":
+        return bench_gemm(args, dev)
     log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal}")
 
     t0 = time.perf_counter()

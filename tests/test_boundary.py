@@ -38,9 +38,10 @@ def declared_functions():
 
 
 def test_headers_declare_the_entry_points():
-    assert [os.path.basename(h) for h in HEADERS] == ["attn_bwd.h", "attn_fwd.h"]
+    assert [os.path.basename(h) for h in HEADERS] == ["attn_bwd.h", "attn_fwd.h", "attn_gemm.h"]
     assert declared_functions() == ["attn_bwd", "attn_fwd", "attn_fwd_abi_version",
-                                    "attn_fwd_ex", "attn_fwd_splitkv", "attn_fwd_strerror"]
+                                    "attn_fwd_ex", "attn_fwd_splitkv", "attn_fwd_strerror",
+                                    "attn_gemm_bf16"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -51,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_codes_match_header(lib):
     text = open(HEADER).read()
-    codes = dict((n, int(v)) for n, v in re.findall(r"ATTN_(\w+)\s*=\s*(\d+)", text))
+    codes = dict((n, int(v)) for n, v in re.findall(r"ATTN_(ERR_\w+|OK)\s*=\s*(\d+)", text))
     for name, value in codes.items():
         assert getattr(af.Status, name) == value
         msg = af.attn_fwd_strerror(value)
@@ -230,3 +231,48 @@ def test_splitkv_split_choice():
     assert af.splitkv_splits(1, 8, 1, 65536, 128) == 64
     assert af.splitkv_splits(16, 16, 4096, 4096, 128) == 1
     assert af.splitkv_splits(1, 1, 1, 100, 64) == 1
+
+
+def call_gemm(M=300, N=264, K=200, layout=0, a=FAKE, b=FAKE, c=FAKE):
+    return af.gemm_raw(a, b, c, M, N, K, layout)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), af.Status.ERR_SHAPE),
+    (dict(N=-8), af.Status.ERR_SHAPE),
+    (dict(K=-8), af.Status.ERR_SHAPE),
+    (dict(N=260), af.Status.ERR_SHAPE),
+    (dict(K=204), af.Status.ERR_SHAPE),
+    (dict(K=1 << 22), af.Status.ERR_SHAPE),
+    (dict(N=1 << 22), af.Status.ERR_SHAPE),
+    (dict(layout=2), af.Status.ERR_SHAPE),
+    (dict(layout=-1), af.Status.ERR_SHAPE),
+    (dict(a=0), af.Status.ERR_NULL),
+    (dict(b=0), af.Status.ERR_NULL),
+    (dict(c=0), af.Status.ERR_NULL),
+    (dict(a=FAKE + 8), af.Status.ERR_ALIGN),
+    (dict(b=FAKE + 2), af.Status.ERR_ALIGN),
+    (dict(c=FAKE + 4), af.Status.ERR_ALIGN),
+])
+def test_gemm_rejects(lib, kw, status):
+    assert call_gemm(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(M=0), dict(N=0), dict(M=0, a=0, b=0, c=0)])
+def test_gemm_empty_problem_is_a_noop(lib, kw):
+    assert call_gemm(**kw) == af.Status.OK
+
+
+def test_gemm_layout_codes_match_header():
+    text = open(os.path.join(ROOT, "include", "attn_gemm.h")).read()
+    codes = dict((n, int(v)) for n, v in re.findall(r"ATTN_GEMM_(\w+)\s*=\s*(\d+)", text))
+    assert codes == {"NN": af.GEMM_NN, "NT": af.GEMM_NT}
+
+
+def test_python_gemm_binding_rejects_bad_input():
+    import torch
+    x = torch.zeros(16, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        af.gemm(x, x)  # CPU tensors
+    with pytest.raises(TypeError):
+        af.gemm(x.float(), x)
