@@ -6,7 +6,7 @@
 //
 // Design:
 //   * a workgroup of 8 waves computes a 256 x 256 tile of C; wave w owns rows
-//     128*(w%2) .. +127 and columns 64*(w/2) .. +63 of it, as 4 x 2 blocks of
+//     64*(w%4) .. +63 and columns 128*(w/4) .. +127 of it, as 2 x 4 blocks of
 //     32 x 32 fp32 accumulators (v_mfma_f32_32x32x16_bf16), two waves per SIMD;
 //   * each block is formed transposed, C^T = B-tile x A-tile^T: the B tile is
 //     the MFMA A operand and the A tile the B operand, so a lane holds one row
@@ -14,8 +14,10 @@
 //     bf16x4 writes;
 //   * K advances 64 at a time; both operand tiles of a step go global -> LDS
 //     through buffer loads that write LDS directly (no register staging),
-//     double-buffered: the loads of step t+1 are issued right after the
-//     barrier that opens step t and land while step t computes;
+//     double-buffered: the loads of step t+1 are issued during step t (all
+//     at once after the barrier for C = A B^T; one pair before each of the
+//     four MFMA k-steps for C = A B, which measured faster there) and land
+//     while step t computes;
 //   * LDS tiles are XOR-swizzled on 16-byte chunks so that every operand read
 //     is bank-conflict free; an NN B tile ([64 k][256 n], n contiguous) is
 //     read with ds_read_b64_tr_b16, which hands each lane 8 consecutive k of
@@ -48,7 +50,8 @@ constexpr int kWave = 64;
 constexpr int kBM = 256, kBN = 256, kBK = 64;  // workgroup tile and K step
 constexpr int kWaves = 8;
 constexpr int kThreads = kWave * kWaves;
-constexpr int kWaveM = 128, kWaveN = 64;  // one wave's part of the tile
+constexpr int kWavesM = 4;                // waves along M (2 along N)
+constexpr int kWaveM = kBM / kWavesM, kWaveN = kBN / (kWaves / kWavesM);  // one wave's part
 constexpr int kMBlocks = kWaveM / 32;
 constexpr int kNBlocks = kWaveN / 32;
 constexpr int kSteps = kBK / 16;           // MFMA k-steps per K step
@@ -104,8 +107,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const __bf16* __
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l32 = lane & 31;
   const int half = lane >> 5;
-  const int wm = wave & 1;   // 128-row half of the tile
-  const int wn = wave >> 1;  // 64-column quarter of the tile
+  const int wm = wave % kWavesM;  // 64-row quarter of the tile
+  const int wn = wave / kWavesM;  // 128-column half of the tile
 
   // Workgroup -> tile.  Logical ids are contiguous per XCD; they run down
   // groups of kGroupM tile rows, column by column.
@@ -148,7 +151,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const __bf16* __
   const unsigned smem_base = (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)smem;
   const unsigned lds_wave = smem_base + wave * kLoadsPerWave * kLoadBytes;
 
-  auto load_step = [&](int kt, int stage) __attribute__((always_inline)) {
+  // Copies of step kt into `stage`: all of them (part < 0) or only the
+  // part-th A and B load of this wave.
+  auto load_step = [&](int kt, int stage, int part) __attribute__((always_inline)) {
     const int k0 = kt * kBK;
     const unsigned dst = __builtin_amdgcn_readfirstlane(lds_wave + stage * kStageBytes);
     {
@@ -157,7 +162,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const __bf16* __
       const i32x4 rsrc = make_rsrc(a + (size_t)m0 * K + k0, bytes);
 #pragma unroll
       for (int it = 0; it < kLoadsPerWave; ++it)
-        load16_to_lds(rsrc, k0 + a_first[it] < K ? a_ld[it] : (int)bytes, dst + it * kLoadBytes);
+        if (part < 0 || part == it)
+          load16_to_lds(rsrc, k0 + a_first[it] < K ? a_ld[it] : (int)bytes, dst + it * kLoadBytes);
     }
     {
       const long long rem = NT ? ((long long)(N - n0) * K - k0) * 2 : ((long long)(K - k0) * N - n0) * 2;
@@ -166,6 +172,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const __bf16* __
       const i32x4 rsrc = make_rsrc(base, bytes);
 #pragma unroll
       for (int it = 0; it < kLoadsPerWave; ++it) {
+        if (part >= 0 && part != it) continue;
         const bool in = NT ? k0 + b_first[it] < K : n0 + b_first[it] < N;
         load16_to_lds(rsrc, in ? b_ld[it] : (int)bytes, dst + kTileBytes + it * kLoadBytes);
       }
@@ -205,15 +212,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const __bf16* __
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  if (n_kt > 0) load_step(0, 0);
+  constexpr bool kSpread = !NT;  // copies spread over the k-steps
+  static_assert(kLoadsPerWave == kSteps, "one A and one B copy per k-step");
+  if (n_kt > 0) load_step(0, 0, -1);
   for (int kt = 0; kt < n_kt; ++kt) {
     wait_lds_dma();
     __syncthreads();  // step kt has landed; everyone is done with step kt-1's stage
-    if (kt + 1 < n_kt) load_step(kt + 1, (kt + 1) & 1);
+    const bool has_next = kt + 1 < n_kt;
+    if (!kSpread && has_next) load_step(kt + 1, (kt + 1) & 1, -1);
     const unsigned char* const sa = smem + (kt & 1) * kStageBytes;
     const unsigned char* const sb = sa + kTileBytes;
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
+      if (kSpread && has_next) load_step(kt + 1, (kt + 1) & 1, st);
       bf16x8 af[kMBlocks], bf[kNBlocks];
 #pragma unroll
       for (int i = 0; i < kMBlocks; ++i)
@@ -237,8 +248,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const __bf16* __
     }
   }
 
-  // Epilogue.  Block (i, j), lane L: row m0 + 128 wm + 32 i + L%32; register
-  // 4q + r: column n0 + 64 wn + 32 j + 8 q + 4 (L/32) + r.
+  // Epilogue.  Block (i, j), lane L: row m0 + 64 wm + 32 i + L%32; register
+  // 4q + r: column n0 + 128 wn + 32 j + 8 q + 4 (L/32) + r.
 #pragma unroll
   for (int i = 0; i < kMBlocks; ++i) {
     const int m = m0 + wm * kWaveM + 32 * i + l32;
