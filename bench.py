@@ -54,6 +54,7 @@ from attention_attn_fwd_08_amd.inputs import (HEADLINE, WORKLOADS, Workload, mak
 # MI355X published dense bf16 MFMA peak: 256 CUs x 4096 flop/clk/CU x 2.4 GHz.
 PEAK_BF16_TFLOPS = 2516.6
 KERNEL_SOURCE = os.path.join(ROOT, "attention_attn_fwd_08_amd", "csrc", "attn_fwd.hip")
+GEMM_SOURCE = os.path.join(ROOT, "attention_attn_fwd_08_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 O_MAX_TOL, O_MEAN_TOL, LSE_MAX_TOL = 2e-2, 2e-3, 1e-3
@@ -63,21 +64,22 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
+def source_sha(path: str) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload: str):
+def measured_traffic(entry_name: str, source: str = KERNEL_SOURCE):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when there is none for this workload or the kernel changed since."""
+    None when it holds no entry of that name or the kernel source changed
+    since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = rec.get("workloads", {}).get(workload)
-    if not entry or rec.get("kernel_source_sha256") != kernel_source_sha():
+    entry = rec.get("entries", {}).get(entry_name)
+    if not entry or entry.get("source_sha256") != source_sha(source):
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -225,7 +227,8 @@ def bench_decode(args, w, dev) -> int:
                    "seed": w.seed, "parallelism": "none", "pass": "decode"},
         "roofline": {"bound": "hbm", "achieved": round(nbytes / (kmean * 1e-3) / 1e9, 1),
                      "peak": 8000.0, "unit": "GB/s",
-                     "frac": round(nbytes / (kmean * 1e-3) / 1e9 / 8000.0, 4), "traffic": None,
+                     "frac": round(nbytes / (kmean * 1e-3) / 1e9 / 8000.0, 4),
+                     "traffic": measured_traffic(f"decode-B{B}-H{H}-Nq1-Nk{Nk}-d{d}"),
                      "kernel_avg_ms": round(kmean, 5), "bytes_per_launch": nbytes,
                      "flop_per_launch": flops,
                      "unit_of_launch": "split kernel and merge kernel"},
@@ -301,7 +304,8 @@ def bench_gemm(args, dev) -> int:
         "roofline": {"bound": "mfma", "achieved": round(flops / (kmean * 1e-3) / 1e12, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / (kmean * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel_avg_ms": round(kmean, 5), "flop_per_launch": flops,
+                     "traffic": measured_traffic(f"gemm-{lay}-M{M}-N{N}-K{K}", GEMM_SOURCE),
+                     "kernel_avg_ms": round(kmean, 5), "flop_per_launch": flops,
                      "algorithmic_hbm_bytes_per_launch": 2 * (M * K + K * N + M * N)},
         "timing": {"kernel_ms_mean": round(kmean, 5), "kernel_ms_median": round(ts[len(ts) // 2], 5),
                    "kernel_ms_min": round(ts[0], 5)},
