@@ -7,7 +7,8 @@
 // Three kernels on one stream:
 //   1. delta_i = rowsum(dO_i * O_i)                     (memory bound)
 //   2. per 128-key block: dV^T += dO^T P and dK^T += Q^T dS while Q and dO
-//      stream through LDS (S = Q K^T, dP = dO V^T, dS = P o (dP - delta))
+//      stream through LDS (S = Q K^T, dP = dO V^T, dS = P o (dP - delta));
+//      at d=128 dV and dK are computed by two workgroups per key block
 //   3. per 128-query block: dQ^T += K^T dS^T while K and V stream through
 //      LDS (S^T = K Q^T, dP^T = V dO^T)
 // Mapping to CDNA4, as in the forward kernel: v_mfma_f32_32x32x16_bf16 with
@@ -192,29 +193,33 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const __bf16* __restrict
 // ---------------------------------------------------------------------------
 // Kernel 2: dK, dV for one 128-key block of one head (32 keys per wave).
 // ---------------------------------------------------------------------------
+constexpr int kQT = 64;  // queries per streamed Q / dO tile
 template <int D>
-struct KvLaunch {
-  static constexpr int kMinBlocks = D == 128 ? 1 : 2;
-};
+constexpr int dkdv_smem_bytes() { return 2 * (2 * kQT * D * 2 + 2 * kQT * 4); }  // 2 stages
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kWaves * kWave, KvLaunch<D>::kMinBlocks)
-void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                     const __bf16* __restrict__ v, const float* __restrict__ lse,
-                     const __bf16* __restrict__ dout, const float* __restrict__ delta,
-                     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int N, float scale, float c) {
+// The work of one workgroup on key block `lid` (head * blocks + block).
+// PART 0: dK and dV together (d=64: several waves per SIMD fit).  PART 1:
+// dV only (S, then dV^T += dO^T P); PART 2: dK only (S and dP, then dK^T +=
+// Q^T dS).  At d=128 the two accumulators together do not fit beside K, V
+// and the scores in the registers of two waves per SIMD, so the parts run as
+// separate workgroups: S is formed twice, but every workgroup runs at two
+// waves per SIMD (measured: about 18 % less time than one combined wave per
+// SIMD).
+template <int D, bool CAUSAL, int PART>
+__device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                          const __bf16* __restrict__ v, const float* __restrict__ lse,
+                                          const __bf16* __restrict__ dout,
+                                          const float* __restrict__ delta, __bf16* __restrict__ dk,
+                                          __bf16* __restrict__ dv, int N, float scale, float c,
+                                          unsigned char* smem, int lid) {
   using G = Geo<D>;
   constexpr int kSteps = G::kSteps;
   constexpr int kDBlocks = G::kDBlocks;
-  // d=128 (one wave per SIMD): 128-query tiles, and the next block's S/dP
-  // MFMAs are issued before this block's exponentials.  d=64 (several waves
-  // per SIMD hide each other): 64-query tiles, blocks one after another.
-  constexpr bool kPipe = D == 128;
-  constexpr int kQT = kPipe ? 128 : 64;       // queries per streamed tile
+  constexpr bool kDoV = PART != 2, kDoK = PART != 1;
   constexpr int kQBlocks = kQT / kRows;       // 32-query blocks per tile
   constexpr int kTileBytes = kQT * G::kRowBytes;
   constexpr int kStageBytes = 2 * kTileBytes + 2 * kQT * 4;  // Q, dO, lse, delta
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStageBytes];
+  static_assert(2 * kStageBytes == dkdv_smem_bytes<D>(), "LDS layout");
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -223,7 +228,6 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int half = lane >> 5;
 
   const int n_kb = (N + kBlock - 1) / kBlock;
-  const int lid = logical_block();
   const int head = lid / n_kb;
   const int kb = lid % n_kb;
   const size_t head_off = (size_t)head * N * D;
@@ -299,7 +303,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
       for (int st = 0; st < kSteps; ++st) {
         sacc = mfma(*reinterpret_cast<const bf16x8*>(qa + ro[st]), kf[st], sacc);
-        pacc = mfma(*reinterpret_cast<const bf16x8*>(da + ro[st]), vf[st], pacc);
+        if (kDoK) pacc = mfma(*reinterpret_cast<const bf16x8*>(da + ro[st]), vf[st], pacc);
       }
     };
     // P = 2^(s*c - lse*log2 e) and dS = P (dP - delta), as bf16 B operands;
@@ -321,8 +325,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             const bool vis = CAUSAL ? (key0 + l32 <= query && query < N) : (query < N);
             p = vis ? p : 0.f;
           }
-          pb[r >> 3][r & 7] = (__bf16)p;
-          sb[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - d4[j]));
+          if (kDoV) pb[r >> 3][r & 7] = (__bf16)p;
+          if (kDoK) sb[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - d4[j]));
         }
       }
     };
@@ -334,38 +338,24 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int b = 0; b < kDBlocks; ++b) {
-          dvt[b] = mfma(read_tr(da, tro[cc][b][0], tro[cc][b][1]), pb[cc], dvt[b]);
-          dkt[b] = mfma(read_tr(qa, tro[cc][b][0], tro[cc][b][1]), sb[cc], dkt[b]);
+          if (kDoV) dvt[b] = mfma(read_tr(da, tro[cc][b][0], tro[cc][b][1]), pb[cc], dvt[b]);
+          if (kDoK) dkt[b] = mfma(read_tr(qa, tro[cc][b][0], tro[cc][b][1]), sb[cc], dkt[b]);
         }
     };
 
     const int qrow_first = qt * kQT;
     const bool interior = (!CAUSAL || qrow_first >= key0 + kRows - 1) && qrow_first + kQT <= N;
-    if (kPipe && interior) {
-      // Every block fully visible: the next block's S and dP go to the MFMA
-      // pipe before this block's exponentials, which then overlap them.
-      f32x16 sa[2], pa[2];
-      sdp(0, sa[0], pa[0]);
 #pragma unroll
-      for (int qb = 0; qb < kQBlocks; ++qb) {
-        if (qb + 1 < kQBlocks) sdp(qb + 1, sa[(qb + 1) & 1], pa[(qb + 1) & 1]);
-        bf16x8 pb[2], sb[2];
-        soft(std::false_type{}, qb, sa[qb & 1], pa[qb & 1], pb, sb);
-        pv(qb, pb, sb);
-      }
-    } else {
-#pragma unroll
-      for (int qb = 0; qb < kQBlocks; ++qb) {
-        const int qrow0 = qrow_first + qb * kRows;
-        if (CAUSAL && qrow0 + kRows - 1 < key0) continue;  // every query precedes every key
-        if (qrow0 >= N) continue;
-        f32x16 sacc, pacc;
-        sdp(qb, sacc, pacc);
-        bf16x8 pb[2], sb[2];
-        if (interior) soft(std::false_type{}, qb, sacc, pacc, pb, sb);
-        else soft(std::true_type{}, qb, sacc, pacc, pb, sb);
-        pv(qb, pb, sb);
-      }
+    for (int qb = 0; qb < kQBlocks; ++qb) {
+      const int qrow0 = qrow_first + qb * kRows;
+      if (CAUSAL && qrow0 + kRows - 1 < key0) continue;  // every query precedes every key
+      if (qrow0 >= N) continue;
+      f32x16 sacc, pacc;
+      sdp(qb, sacc, pacc);
+      bf16x8 pb[2], sb[2];
+      if (interior) soft(std::false_type{}, qb, sacc, pacc, pb, sb);
+      else soft(std::true_type{}, qb, sacc, pacc, pb, sb);
+      pv(qb, pb, sb);
     }
   }
 
@@ -385,10 +375,37 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           kv4[r] = (__bf16)(dkt[b][4 * j + r] * scale);
           vv4[r] = (__bf16)dvt[b][4 * j + r];
         }
-        *reinterpret_cast<bf16x4*>(kr + 32 * b + 8 * j + 4 * half) = kv4;
-        *reinterpret_cast<bf16x4*>(vr + 32 * b + 8 * j + 4 * half) = vv4;
+        if (kDoK) *reinterpret_cast<bf16x4*>(kr + 32 * b + 8 * j + 4 * half) = kv4;
+        if (kDoV) *reinterpret_cast<bf16x4*>(vr + 32 * b + 8 * j + 4 * half) = vv4;
       }
   }
+}
+
+// d=64: dK and dV in one workgroup per key block.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kWaves * kWave, 2)
+void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                     const __bf16* __restrict__ v, const float* __restrict__ lse,
+                     const __bf16* __restrict__ dout, const float* __restrict__ delta,
+                     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int N, float scale, float c) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[dkdv_smem_bytes<D>()];
+  dkdv_body<D, CAUSAL, 0>(q, k, v, lse, dout, delta, dk, dv, N, scale, c, smem, logical_block());
+}
+
+// d=128: two workgroups per key block, one for dV and one for dK.  Logical
+// ids 2b and 2b+1 are the two parts of key block b, so they run side by side
+// on one XCD and share the Q and dO tiles in its L2.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kWaves * kWave, 2)
+void bwd_dkdv_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                           const __bf16* __restrict__ v, const float* __restrict__ lse,
+                           const __bf16* __restrict__ dout, const float* __restrict__ delta,
+                           __bf16* __restrict__ dk, __bf16* __restrict__ dv, int N, float scale,
+                           float c) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[dkdv_smem_bytes<D>()];
+  const int lid = logical_block();
+  if (lid & 1) dkdv_body<D, CAUSAL, 2>(q, k, v, lse, dout, delta, dk, dv, N, scale, c, smem, lid >> 1);
+  else dkdv_body<D, CAUSAL, 1>(q, k, v, lse, dout, delta, dk, dv, N, scale, c, smem, lid >> 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -552,10 +569,16 @@ int launch(const void* q, const void* k, const void* v, const void* o, const flo
   hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream,
                      static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), delta, rows);
   const int n_blk = (N + kBlock - 1) / kBlock;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_blk * BH), dim3(kWaves * kWave), 0, stream,
-                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                     static_cast<const __bf16*>(v), lse, static_cast<const __bf16*>(dout), delta,
-                     static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), N, scale, c);
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((bwd_dkdv_split_kernel<D, CAUSAL>), dim3(2 * n_blk * BH), dim3(kWaves * kWave), 0,
+                       stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                       static_cast<const __bf16*>(v), lse, static_cast<const __bf16*>(dout), delta,
+                       static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), N, scale, c);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_blk * BH), dim3(kWaves * kWave), 0, stream,
+                       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                       static_cast<const __bf16*>(v), lse, static_cast<const __bf16*>(dout), delta,
+                       static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), N, scale, c);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_blk * BH), dim3(kWaves * kWave), 0, stream,
                      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), lse, static_cast<const __bf16*>(dout), delta,
@@ -574,7 +597,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   if (!(scale > 0.0f) || !isfinite(scale)) return ATTN_ERR_SCALE;
   const int64_t bh = (int64_t)B * H;
   if (bh > INT32_MAX) return ATTN_ERR_SHAPE;
-  if (bh * (((int64_t)N + kBlock - 1) / kBlock) > INT32_MAX) return ATTN_ERR_SHAPE;  // grid
+  if (2 * bh * (((int64_t)N + kBlock - 1) / kBlock) > INT32_MAX) return ATTN_ERR_SHAPE;  // grid
   if ((int64_t)N * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;  // one head's bytes fit an int
   if (bh * N > (int64_t)INT32_MAX * 32) return ATTN_ERR_SHAPE;  // delta grid
   if (bh == 0 || N == 0) return ATTN_OK;
