@@ -84,6 +84,18 @@ def measured_traffic(entry_name: str, source: str = KERNEL_SOURCE):
     return entry.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), for the baseline record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def sample_sclk_mhz(run_for_s: float, launch) -> float | None:
     """Median shader clock (MHz) that rocm-smi reports while `launch` runs back
     to back for about `run_for_s` seconds; None when rocm-smi is unavailable."""
@@ -138,6 +150,7 @@ def cpu_baseline(w, q, k, v, target_gflop: float, threads: int):
         "value": flop / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu": cpu_model(),
         "kind": "oracle",
         "sample": (f"{rows.size} query rows of {w.name} ({per_head} per head, every head; "
                    f"{flop / 1e9:.1f} GFLOP fp64) in {dt:.2f} s wall on {threads} threads"),
@@ -155,7 +168,7 @@ def cpu_baseline_bwd(w, q, k, v, dout, threads: int):
     grads = oracle.attention_bwd(*sub, w.causal, w.scale, threads=1)
     dt = time.perf_counter() - t0
     flop = 10.0 * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
-    rec = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+    rec = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "cpu": cpu_model(), "kind": "oracle",
            "sample": (f"backward of head (0,0) of {w.name} ({flop / 1e9:.1f} GFLOP by the "
                       f"10*N^2*d count; the oracle forms full N x N matrices) in {dt:.2f} s "
                       f"on 1 thread")}
@@ -330,6 +343,7 @@ def bench_gemm(args, dev) -> int:
         sample_flop = 2.0 * rows.size * N * K
         result["cpu_baseline"] = {
             "value": sample_flop / dt / 1e12, "unit": "TFLOP/s", "cores": min(threads, rows.size),
+            "cpu": cpu_model(),
             "kind": "oracle",
             "sample": f"{rows.size} rows of C ({sample_flop / 1e9:.1f} GFLOP fp64) in {dt:.2f} s wall"}
         got = bf16_bits_to_f32(c[torch.as_tensor(rows, device=dev)].view(torch.int16).cpu().numpy()
