@@ -5,9 +5,9 @@ TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.  Only ``tests/``,
 this package.  It shares no code with the HIP library and never imports it.
 
 The arithmetic lives in ``attn_oracle.c`` (forward), ``attn_bwd_oracle.c``
-(backward: the derivative of the same definition, full matrices per head) and
-``gemm_oracle.c`` (the plain matrix product), all single-threaded C, fp64,
-with libm exp/log.  This module only compiles that file with gcc, loads it with ctypes and
+and ``attn_bwd_ex_oracle.c`` (backward: the derivative of the same definition,
+full matrices per head, square and general shapes) and ``gemm_oracle.c`` (the
+plain matrix product), all single-threaded C, fp64, with libm exp/log.  This module only compiles that file with gcc, loads it with ctypes and
 hands it buffers.  ``threads > 1`` splits the list of query rows between host
 threads, each running the same single-threaded C routine on its own rows (the
 rows are independent, so the result does not depend on the split).
@@ -34,8 +34,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "attn_oracle.c")
-SOURCES = (SOURCE, os.path.join(_HERE, "attn_bwd_oracle.c"), os.path.join(_HERE, "gemm_oracle.c"))
+SOURCES = (SOURCE, os.path.join(_HERE, "attn_bwd_oracle.c"), os.path.join(_HERE, "gemm_oracle.c"),
+           os.path.join(_HERE, "attn_bwd_ex_oracle.c"))
 GEMM_SOURCE = SOURCES[2]
+BWD_EX_SOURCE = SOURCES[3]
 LIBRARY = os.path.join(_HERE, "libattn_oracle.so")
 
 _lock = threading.Lock()
@@ -85,6 +87,18 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
             f64p, f64p, f64p, f64p, i64, i64, ctypes.c_int, ctypes.c_double,
             f64p, f64p, f64p, f64p, f64p, f64p, f64p]
         lib.attn_bwd_oracle_head_f64.restype = ctypes.c_int
+    if hasattr(lib, "attn_bwd_oracle_heads_ex"):
+        lib.attn_bwd_oracle_heads_ex.argtypes = [
+            u16p, u16p, u16p, u16p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_double, i64, i64,
+            f64p, f64p, f64p, f64p]
+        lib.attn_bwd_oracle_heads_ex.restype = ctypes.c_int
+        lib.attn_fwd_oracle_head_ex_f64.argtypes = [
+            f64p, f64p, f64p, i64, i64, i64, ctypes.c_int, ctypes.c_double, f64p, f64p, f64p]
+        lib.attn_fwd_oracle_head_ex_f64.restype = ctypes.c_int
+        lib.attn_bwd_oracle_head_ex_f64.argtypes = [
+            f64p, f64p, f64p, f64p, i64, i64, i64, ctypes.c_int, ctypes.c_double,
+            f64p, f64p, f64p, f64p, f64p, f64p, f64p]
+        lib.attn_bwd_oracle_head_ex_f64.restype = ctypes.c_int
     if hasattr(lib, "gemm_oracle_rows"):
         lib.gemm_oracle_rows.argtypes = [u16p, u16p, i64, i64, i64, ctypes.c_int,
                                          ctypes.POINTER(ctypes.c_int64), i64, f64p]
@@ -292,6 +306,81 @@ def attention_ex(q, k, v, causal: bool, scale: float, threads: int = 1,
     if any(s != 0 for s in statuses):
         raise RuntimeError(f"oracle failed with status {statuses}")
     return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
+
+
+def attention_bwd_ex(q, k, v, dout, causal: bool, scale: float, threads: int = 1,
+                     lib: ctypes.CDLL | None = None):
+    """Gradients of sum(O * dout) for q, dout [B,H,Nq,d] against k, v
+    [B,H,Nk,d] (bf16 bits), bottom-right causal.  Returns (dq, dk, dv, delta)
+    in fp64; rows that see no key have dq = 0 and delta = 0."""
+    for name, a in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        if not isinstance(a, np.ndarray) or a.dtype != np.uint16 or a.ndim != 4:
+            raise TypeError(f"{name} must be a 4-D numpy uint16 array of bf16 bits")
+    q, k, v, dout = (np.ascontiguousarray(a) for a in (q, k, v, dout))
+    B, H, Nq, d = q.shape
+    if k.shape != v.shape or k.shape[:2] != (B, H) or k.shape[3] != d or dout.shape != q.shape:
+        raise ValueError("k, v must be [B, H, Nk, d] and dout shaped like q")
+    Nk = k.shape[2]
+    BH = B * H
+    lib = lib or load()
+    dq = np.zeros((B, H, Nq, d)); dk = np.zeros((B, H, Nk, d)); dv = np.zeros((B, H, Nk, d))
+    delta = np.zeros((B, H, Nq))
+    threads = max(1, min(int(threads), BH))
+    bounds = np.linspace(0, BH, threads + 1).astype(np.int64)
+
+    def run(part):
+        lo, hi = int(bounds[part]), int(bounds[part + 1])
+        if hi <= lo:
+            return 0
+        return lib.attn_bwd_oracle_heads_ex(
+            _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
+            _ptr(dout, ctypes.c_uint16), BH, Nq, Nk, d, int(bool(causal)), float(scale), lo, hi,
+            _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double), _ptr(dv, ctypes.c_double),
+            _ptr(delta, ctypes.c_double))
+
+    if threads == 1:
+        statuses = [run(0)]
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as pool:
+            statuses = list(pool.map(run, range(threads)))
+    if any(s != 0 for s in statuses):
+        raise RuntimeError(f"oracle failed with status {statuses}")
+    return dq, dk, dv, delta
+
+
+def forward_head_ex_f64(q, k, v, causal: bool, scale: float, lib: ctypes.CDLL | None = None):
+    """General-shape forward of one head on float64 q [Nq, d], k, v [Nk, d]."""
+    q, k, v = (np.ascontiguousarray(a, dtype=np.float64) for a in (q, k, v))
+    Nq, d = q.shape
+    Nk = k.shape[0]
+    lib = lib or load()
+    o = np.zeros((Nq, d)); lse = np.zeros(Nq); p = np.zeros((Nq, max(Nk, 1)))
+    st = lib.attn_fwd_oracle_head_ex_f64(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
+                                         _ptr(v, ctypes.c_double), Nq, Nk, d, int(bool(causal)),
+                                         float(scale), _ptr(o, ctypes.c_double),
+                                         _ptr(lse, ctypes.c_double), _ptr(p, ctypes.c_double))
+    if st != 0:
+        raise RuntimeError(f"oracle failed with status {st}")
+    return o, lse, p[:, :Nk]
+
+
+def backward_head_ex_f64(q, k, v, dout, causal: bool, scale: float,
+                         lib: ctypes.CDLL | None = None):
+    """General-shape backward of one head on float64 inputs: (dq, dk, dv, delta, o, lse)."""
+    q, k, v, dout = (np.ascontiguousarray(a, dtype=np.float64) for a in (q, k, v, dout))
+    Nq, d = q.shape
+    Nk = k.shape[0]
+    lib = lib or load()
+    dq = np.zeros((Nq, d)); dk = np.zeros((Nk, d)); dv = np.zeros((Nk, d))
+    delta = np.zeros(Nq); o = np.zeros((Nq, d)); lse = np.zeros(Nq)
+    scratch = np.zeros(2 * Nq * Nk + 1)
+    f = lambda a: _ptr(a, ctypes.c_double)  # noqa: E731
+    st = lib.attn_bwd_oracle_head_ex_f64(f(q), f(k), f(v), f(dout), Nq, Nk, d, int(bool(causal)),
+                                         float(scale), f(dq), f(dk), f(dv), f(delta), f(o), f(lse),
+                                         f(scratch))
+    if st != 0:
+        raise RuntimeError(f"oracle failed with status {st}")
+    return dq, dk, dv, delta, o, lse
 
 
 # ---------------------------------------------------------------------------
