@@ -29,7 +29,7 @@ import threading
 
 __all__ = ["attn_fwd", "attn_fwd_raw", "attn_fwd_ex", "attn_fwd_ex_raw", "attn_fwd_splitkv",
            "attn_fwd_splitkv_raw", "splitkv_splits", "attn_bwd",
-           "attn_bwd_raw", "gemm", "gemm_raw", "GEMM_NN", "GEMM_NT", "attn_fwd_strerror",
+           "attn_bwd_raw", "attn_bwd_ex", "attn_bwd_ex_raw", "gemm", "gemm_raw", "GEMM_NN", "GEMM_NT", "attn_fwd_strerror",
            "load_library", "LIBRARY", "Status", "AttnError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +91,8 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.attn_fwd_splitkv.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [vp] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float, vp]
     lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_ex.argtypes = [vp] * 10 + [ctypes.c_int] * 6 + [ctypes.c_float, vp]
+    lib.attn_bwd_ex.restype = ctypes.c_int
     lib.attn_gemm_bf16.argtypes = [vp] * 3 + [ctypes.c_int] * 4 + [vp]
     lib.attn_gemm_bf16.restype = ctypes.c_int
     return lib
@@ -174,6 +176,58 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = 
         status = attn_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                               lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                               dv.data_ptr(), delta.data_ptr(), B, H, N, d, causal, scale, stream)
+    if status != Status.OK:
+        raise AttnError(status, attn_fwd_strerror(status))
+    return dq, dk, dv, delta
+
+
+def attn_bwd_ex_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, do_ptr: int,
+                    dq_ptr: int, dk_ptr: int, dv_ptr: int, delta_ptr: int,
+                    B: int, H: int, Nq: int, Nk: int, d: int, causal: bool, scale: float,
+                    stream: int = 0) -> int:
+    """Call ``attn_bwd_ex`` with raw integer addresses; returns the status."""
+    lib = load_library()
+    ptrs = [p or None for p in (q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr,
+                                dv_ptr, delta_ptr)]
+    return lib.attn_bwd_ex(*ptrs, int(B), int(H), int(Nq), int(Nk), int(d), int(bool(causal)),
+                           float(scale), stream or None)
+
+
+def attn_bwd_ex(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+                dq=None, dk=None, dv=None, delta=None):
+    """Backward of :func:`attn_fwd_ex`: q, o, dout [B, H, Nq, d], k, v
+    [B, H, Nk, d], lse [B, H, Nq]; bottom-right causal.  Returns
+    ``(dq, dk, dv, delta)``."""
+    import torch
+
+    _check_bf16("q", q, None, None)
+    B, H, Nq, d = q.shape
+    dev = q.device
+    _check_bf16("k", k, None, dev)
+    if k.shape[:2] != (B, H) or k.shape[3] != d:
+        raise ValueError("k must be [B, H, Nk, d] with q's B, H and d")
+    _check_bf16("v", v, k.shape, dev)
+    for name, t in (("o", o), ("dout", dout)):
+        _check_bf16(name, t, q.shape, dev)
+    Nk = k.shape[2]
+    _check_f32("lse", lse, (B, H, Nq), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(k) if dv is None else dv
+    _check_bf16("dq", dq, q.shape, dev)
+    _check_bf16("dk", dk, k.shape, dev)
+    _check_bf16("dv", dv, k.shape, dev)
+    if delta is None:
+        delta = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    _check_f32("delta", delta, (B, H, Nq), dev)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        status = attn_bwd_ex_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                 lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                 dv.data_ptr(), delta.data_ptr(), B, H, Nq, Nk, d, causal, scale,
+                                 stream)
     if status != Status.OK:
         raise AttnError(status, attn_fwd_strerror(status))
     return dq, dk, dv, delta

@@ -205,13 +205,16 @@ constexpr int dkdv_smem_bytes() { return 2 * (2 * kQT * D * 2 + 2 * kQT * 4); } 
 // separate workgroups: S is formed twice, but every workgroup runs at two
 // waves per SIMD (measured: about 18 % less time than one combined wave per
 // SIMD).
-template <int D, bool CAUSAL, int PART>
+//
+// GENERAL: Nq queries against Nk keys, causal mask offset by `off` (key j
+// visible to query i iff j <= i + off); otherwise Nk = Nq and off = 0.
+template <int D, bool CAUSAL, int PART, bool GENERAL>
 __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                           const __bf16* __restrict__ v, const float* __restrict__ lse,
                                           const __bf16* __restrict__ dout,
                                           const float* __restrict__ delta, __bf16* __restrict__ dk,
-                                          __bf16* __restrict__ dv, int N, float scale, float c,
-                                          unsigned char* smem, int lid) {
+                                          __bf16* __restrict__ dv, int Nq, int nk_arg, int off_arg,
+                                          float scale, float c, unsigned char* smem, int lid) {
   using G = Geo<D>;
   constexpr int kSteps = G::kSteps;
   constexpr int kDBlocks = G::kDBlocks;
@@ -227,23 +230,26 @@ __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  const int n_kb = (N + kBlock - 1) / kBlock;
+  const int Nk = GENERAL ? nk_arg : Nq;
+  const int off = GENERAL ? off_arg : 0;
+  const int n_kb = (Nk + kBlock - 1) / kBlock;
   const int head = lid / n_kb;
   const int kb = lid % n_kb;
-  const size_t head_off = (size_t)head * N * D;
-  const __bf16* const qh = q + head_off;
-  const __bf16* const doh = dout + head_off;
-  const float* const lseh = lse + (size_t)head * N;
-  const float* const dlth = delta + (size_t)head * N;
+  const size_t q_off = (size_t)head * Nq * D;   // q, dO: [head, Nq, D]
+  const size_t kv_off = (size_t)head * Nk * D;  // k, v, dK, dV: [head, Nk, D]
+  const __bf16* const qh = q + q_off;
+  const __bf16* const doh = dout + q_off;
+  const float* const lseh = lse + (size_t)head * Nq;
+  const float* const dlth = delta + (size_t)head * Nq;
   const int key0 = kb * kBlock + wave * kRows;  // this wave's first key
 
-  // K^T and V^T as B operands: lane L holds key key0 + L%32 (rows past N: any
-  // valid row; their outputs are not stored), features 16*st + 8*(L/32)..+7.
+  // K^T and V^T as B operands: lane L holds key key0 + L%32 (rows past Nk:
+  // any valid row; their outputs are not stored), features 16*st + 8*(L/32)..+7.
   bf16x8 kf[kSteps], vf[kSteps];
   {
-    const int row = min(key0 + l32, N - 1);
-    const __bf16* kr = k + head_off + (size_t)row * D + 8 * half;
-    const __bf16* vr = v + head_off + (size_t)row * D + 8 * half;
+    const int row = min(key0 + l32, Nk - 1);
+    const __bf16* kr = k + kv_off + (size_t)row * D + 8 * half;
+    const __bf16* vr = v + kv_off + (size_t)row * D + 8 * half;
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
       kf[st] = *reinterpret_cast<const bf16x8*>(kr + 16 * st);
@@ -267,18 +273,19 @@ __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __
 #pragma unroll
       for (int h = 0; h < 2; ++h) tro[cc][b][h] = tr_off<D>(lane, h, b, cc);
 
-  // Query tiles that see at least one key of the block.
-  const int qt_first = CAUSAL ? (kb * kBlock) / kQT : 0;
-  const int n_qt = (N + kQT - 1) / kQT;
+  // Query tiles that see at least one key of the block (query i sees the
+  // block's first key iff i >= kb*kBlock - off).
+  const int qt_first = CAUSAL ? max(kb * kBlock - off, 0) / kQT : 0;
+  const int n_qt = (Nq + kQT - 1) / kQT;
   auto stage_ptr = [&](int s) __attribute__((always_inline)) { return smem + s * kStageBytes; };
   auto issue = [&](int qt, int s) __attribute__((always_inline)) {
     unsigned char* st_base = stage_ptr(s);
     const int row0 = qt * kQT;
-    copy_tile<D, kQT>(qh, N, row0, lds_addr(st_base), wave, lane);
-    copy_tile<D, kQT>(doh, N, row0, lds_addr(st_base + kTileBytes), wave, lane);
+    copy_tile<D, kQT>(qh, Nq, row0, lds_addr(st_base), wave, lane);
+    copy_tile<D, kQT>(doh, Nq, row0, lds_addr(st_base + kTileBytes), wave, lane);
     if (wave == 0) {
-      copy_vec<kQT>(lseh, N, row0, lds_addr(st_base + 2 * kTileBytes), lane);
-      copy_vec<kQT>(dlth, N, row0, lds_addr(st_base + 2 * kTileBytes + kQT * 4), lane);
+      copy_vec<kQT>(lseh, Nq, row0, lds_addr(st_base + 2 * kTileBytes), lane);
+      copy_vec<kQT>(dlth, Nq, row0, lds_addr(st_base + 2 * kTileBytes + kQT * 4), lane);
     }
   };
   if (qt_first < n_qt) issue(qt_first, 0);
@@ -320,9 +327,9 @@ __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __
         for (int j = 0; j < 4; ++j) {
           const int r = 4 * g + j;
           float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -l4[j] * kLog2e));
-          if constexpr (MASK) {
+          if constexpr (MASK) {  // (a row that sees no key has lse = -inf: p is selected away)
             const int query = qt * kQT + qi + j;
-            const bool vis = CAUSAL ? (key0 + l32 <= query && query < N) : (query < N);
+            const bool vis = CAUSAL ? (key0 + l32 <= query + off && query < Nq) : (query < Nq);
             p = vis ? p : 0.f;
           }
           if (kDoV) pb[r >> 3][r & 7] = (__bf16)p;
@@ -344,12 +351,12 @@ __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __
     };
 
     const int qrow_first = qt * kQT;
-    const bool interior = (!CAUSAL || qrow_first >= key0 + kRows - 1) && qrow_first + kQT <= N;
+    const bool interior = (!CAUSAL || qrow_first + off >= key0 + kRows - 1) && qrow_first + kQT <= Nq;
 #pragma unroll
     for (int qb = 0; qb < kQBlocks; ++qb) {
       const int qrow0 = qrow_first + qb * kRows;
-      if (CAUSAL && qrow0 + kRows - 1 < key0) continue;  // every query precedes every key
-      if (qrow0 >= N) continue;
+      if (CAUSAL && qrow0 + kRows - 1 + off < key0) continue;  // no query sees a key of the wave
+      if (qrow0 >= Nq) continue;
       f32x16 sacc, pacc;
       sdp(qb, sacc, pacc);
       bf16x8 pb[2], sb[2];
@@ -362,9 +369,9 @@ __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __
   // Epilogue: lane = key; registers 4j..4j+3 of block b are features
   // 32b + 8j + 4*(L/32) + 0..3.
   const int key = key0 + l32;
-  if (key < N) {
-    __bf16* const kr = dk + head_off + (size_t)key * D;
-    __bf16* const vr = dv + head_off + (size_t)key * D;
+  if (key < Nk) {
+    __bf16* const kr = dk + kv_off + (size_t)key * D;
+    __bf16* const vr = dv + kv_off + (size_t)key * D;
 #pragma unroll
     for (int b = 0; b < kDBlocks; ++b)
 #pragma unroll
@@ -382,41 +389,47 @@ __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __
 }
 
 // d=64: dK and dV in one workgroup per key block.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool GENERAL>
 __global__ __launch_bounds__(kWaves * kWave, 2)
 void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, const float* __restrict__ lse,
                      const __bf16* __restrict__ dout, const float* __restrict__ delta,
-                     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int N, float scale, float c) {
+                     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Nq, int Nk, int off,
+                     float scale, float c) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[dkdv_smem_bytes<D>()];
-  dkdv_body<D, CAUSAL, 0>(q, k, v, lse, dout, delta, dk, dv, N, scale, c, smem, logical_block());
+  dkdv_body<D, CAUSAL, 0, GENERAL>(q, k, v, lse, dout, delta, dk, dv, Nq, Nk, off, scale, c, smem,
+                                   logical_block());
 }
 
 // d=128: two workgroups per key block, one for dV and one for dK.  Logical
 // ids 2b and 2b+1 are the two parts of key block b, so they run side by side
 // on one XCD and share the Q and dO tiles in its L2.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool GENERAL>
 __global__ __launch_bounds__(kWaves * kWave, 2)
 void bwd_dkdv_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                            const __bf16* __restrict__ v, const float* __restrict__ lse,
                            const __bf16* __restrict__ dout, const float* __restrict__ delta,
-                           __bf16* __restrict__ dk, __bf16* __restrict__ dv, int N, float scale,
-                           float c) {
+                           __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Nq, int Nk, int off,
+                           float scale, float c) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[dkdv_smem_bytes<D>()];
   const int lid = logical_block();
-  if (lid & 1) dkdv_body<D, CAUSAL, 2>(q, k, v, lse, dout, delta, dk, dv, N, scale, c, smem, lid >> 1);
-  else dkdv_body<D, CAUSAL, 1>(q, k, v, lse, dout, delta, dk, dv, N, scale, c, smem, lid >> 1);
+  if (lid & 1)
+    dkdv_body<D, CAUSAL, 2, GENERAL>(q, k, v, lse, dout, delta, dk, dv, Nq, Nk, off, scale, c, smem,
+                                     lid >> 1);
+  else
+    dkdv_body<D, CAUSAL, 1, GENERAL>(q, k, v, lse, dout, delta, dk, dv, Nq, Nk, off, scale, c, smem,
+                                     lid >> 1);
 }
 
 // ---------------------------------------------------------------------------
 // Kernel 3: dQ for one 128-query block of one head (32 queries per wave).
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool GENERAL>
 __global__ __launch_bounds__(kWaves * kWave, 2)
 void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                    const __bf16* __restrict__ v, const float* __restrict__ lse,
                    const __bf16* __restrict__ dout, const float* __restrict__ delta,
-                   __bf16* __restrict__ dq, int N, float scale, float c) {
+                   __bf16* __restrict__ dq, int Nq, int nk_arg, int off_arg, float scale, float c) {
   using G = Geo<D>;
   constexpr int kSteps = G::kSteps;
   constexpr int kDBlocks = G::kDBlocks;
@@ -430,30 +443,34 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  const int n_qb = (N + kBlock - 1) / kBlock;
+  const int Nk = GENERAL ? nk_arg : Nq;
+  const int off = GENERAL ? off_arg : 0;
+  const int n_qb = (Nq + kBlock - 1) / kBlock;
   const int lid = logical_block();
   const int head = lid / n_qb;
   const int qb = CAUSAL ? n_qb - 1 - lid % n_qb : lid % n_qb;  // causal: longest first
-  const size_t head_off = (size_t)head * N * D;
-  const __bf16* const kh = k + head_off;
-  const __bf16* const vh = v + head_off;
+  const size_t q_off = (size_t)head * Nq * D;
+  const size_t kv_off = (size_t)head * Nk * D;
+  const __bf16* const kh = k + kv_off;
+  const __bf16* const vh = v + kv_off;
   const int q0 = qb * kBlock + wave * kRows;  // this wave's first query
 
-  // Q^T and dO^T as B operands: lane L holds query q0 + L%32 (rows past N: any
-  // valid row, not stored), features 16*st + 8*(L/32)..+7.
+  // Q^T and dO^T as B operands: lane L holds query q0 + L%32 (rows past Nq:
+  // any valid row, not stored), features 16*st + 8*(L/32)..+7.
   bf16x8 qf[kSteps], gf[kSteps];
-  const int row = min(q0 + l32, N - 1);
+  const int row = min(q0 + l32, Nq - 1);
   {
-    const __bf16* qr = q + head_off + (size_t)row * D + 8 * half;
-    const __bf16* gr = dout + head_off + (size_t)row * D + 8 * half;
+    const __bf16* qr = q + q_off + (size_t)row * D + 8 * half;
+    const __bf16* gr = dout + q_off + (size_t)row * D + 8 * half;
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
       qf[st] = *reinterpret_cast<const bf16x8*>(qr + 16 * st);
       gf[st] = *reinterpret_cast<const bf16x8*>(gr + 16 * st);
     }
   }
-  const float lse2 = lse[(size_t)head * N + row] * kLog2e;
-  const float dlt = delta[(size_t)head * N + row];
+  // (a row that sees no key has lse = -inf; every key is masked for it)
+  const float lse2 = lse[(size_t)head * Nq + row] * kLog2e;
+  const float dlt = delta[(size_t)head * Nq + row];
   const int query = q0 + l32;
 
   f32x16 dqt[kDBlocks];  // dQ^T: [d, queries]; lane = query
@@ -473,13 +490,13 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
       for (int h = 0; h < 2; ++h) tro[cc][b][h] = tr_off<D>(lane, h, b, cc);
 
-  const int kv_end = CAUSAL ? min((qb + 1) * kBlock, N) : N;
-  const int n_kt = (kv_end + kTile - 1) / kTile;
-  const int wave_last_key = CAUSAL ? min(q0 + kRows - 1, N - 1) : N - 1;
+  const int kv_end = CAUSAL ? min((qb + 1) * kBlock + off, Nk) : Nk;
+  const int n_kt = kv_end > 0 ? (kv_end + kTile - 1) / kTile : 0;
+  const int wave_last_key = CAUSAL ? min(q0 + kRows - 1 + off, Nk - 1) : Nk - 1;
   auto issue = [&](int kt, int s) __attribute__((always_inline)) {
     unsigned char* st_base = smem + s * kStageBytes;
-    copy_tile<D>(kh, N, kt * kTile, lds_addr(st_base), wave, lane);
-    copy_tile<D>(vh, N, kt * kTile, lds_addr(st_base + kTileBytes), wave, lane);
+    copy_tile<D>(kh, Nk, kt * kTile, lds_addr(st_base), wave, lane);
+    copy_tile<D>(vh, Nk, kt * kTile, lds_addr(st_base + kTileBytes), wave, lane);
   };
   if (n_kt > 0) issue(0, 0);
 
@@ -490,7 +507,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     if (kt + 1 < n_kt) issue(kt + 1, s ^ 1);
     const unsigned char* const k_lds = smem + s * kStageBytes;
     const unsigned char* const v_lds = k_lds + kTileBytes;
-    const bool partial = kt * kTile + kTile - 1 > wave_last_key || (CAUSAL && kt * kTile + kTile - 1 > q0);
+    const bool partial =
+        kt * kTile + kTile - 1 > wave_last_key || (CAUSAL && kt * kTile + kTile - 1 > q0 + off);
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       const int key0 = kt * kTile + sb * kRows;
@@ -513,7 +531,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -lse2));
         if (partial) {
           const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = key < N && (!CAUSAL || key <= query);
+          const bool vis = key < Nk && (!CAUSAL || key <= query + off);
           p = vis ? p : 0.f;
         }
         sbf[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - dlt));
@@ -527,8 +545,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
   }
 
-  if (query < N) {
-    __bf16* const qr = dq + head_off + (size_t)query * D;
+  if (query < Nq) {
+    __bf16* const qr = dq + q_off + (size_t)query * D;
 #pragma unroll
     for (int b = 0; b < kDBlocks; ++b)
 #pragma unroll
@@ -560,30 +578,85 @@ bool device_is_gfx950(int dev) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-template <int D, bool CAUSAL>
+// Nq, Nk >= 0 (square: Nq = Nk); a launch with an empty grid is skipped.
+template <int D, bool CAUSAL, bool GENERAL>
 int launch(const void* q, const void* k, const void* v, const void* o, const float* lse,
-           const void* dout, void* dq, void* dk, void* dv, float* delta, int BH, int N, float scale,
-           hipStream_t stream) {
-  const long long rows = (long long)BH * N;
+           const void* dout, void* dq, void* dk, void* dv, float* delta, int BH, int Nq, int Nk,
+           float scale, hipStream_t stream) {
+  const long long rows = (long long)BH * Nq;
   const float c = scale * kLog2e;
-  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream,
-                     static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), delta, rows);
-  const int n_blk = (N + kBlock - 1) / kBlock;
-  if constexpr (D == 128)
-    hipLaunchKernelGGL((bwd_dkdv_split_kernel<D, CAUSAL>), dim3(2 * n_blk * BH), dim3(kWaves * kWave), 0,
+  const int off = Nk - Nq;
+  if (rows > 0)
+    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream,
+                       static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), delta, rows);
+  const int n_kblk = (Nk + kBlock - 1) / kBlock;
+  const int n_qblk = (Nq + kBlock - 1) / kBlock;
+  if (n_kblk > 0) {
+    if constexpr (D == 128)
+      hipLaunchKernelGGL((bwd_dkdv_split_kernel<D, CAUSAL, GENERAL>), dim3(2 * n_kblk * BH),
+                         dim3(kWaves * kWave), 0, stream, static_cast<const __bf16*>(q),
+                         static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), lse,
+                         static_cast<const __bf16*>(dout), delta, static_cast<__bf16*>(dk),
+                         static_cast<__bf16*>(dv), Nq, Nk, off, scale, c);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, GENERAL>), dim3(n_kblk * BH), dim3(kWaves * kWave),
+                         0, stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                         static_cast<const __bf16*>(v), lse, static_cast<const __bf16*>(dout), delta,
+                         static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), Nq, Nk, off, scale, c);
+  }
+  if (n_qblk > 0)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, GENERAL>), dim3(n_qblk * BH), dim3(kWaves * kWave), 0,
                        stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                        static_cast<const __bf16*>(v), lse, static_cast<const __bf16*>(dout), delta,
-                       static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), N, scale, c);
-  else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_blk * BH), dim3(kWaves * kWave), 0, stream,
-                       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                       static_cast<const __bf16*>(v), lse, static_cast<const __bf16*>(dout), delta,
-                       static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), N, scale, c);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_blk * BH), dim3(kWaves * kWave), 0, stream,
-                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                     static_cast<const __bf16*>(v), lse, static_cast<const __bf16*>(dout), delta,
-                     static_cast<__bf16*>(dq), N, scale, c);
+                       static_cast<__bf16*>(dq), Nq, Nk, off, scale, c);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+namespace {
+
+// Argument checks shared by both entry points (before any HIP call).
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dout, const void* dq, const void* dk, const void* dv, const float* delta,
+              int B, int H, int Nq, int Nk, int d, float scale, bool* nothing) {
+  *nothing = false;
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (!(scale > 0.0f) || !isfinite(scale)) return ATTN_ERR_SCALE;
+  const int64_t bh = (int64_t)B * H;
+  if (bh > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (2 * bh * (((int64_t)Nk + kBlock - 1) / kBlock) > INT32_MAX) return ATTN_ERR_SHAPE;  // grids
+  if (bh * (((int64_t)Nq + kBlock - 1) / kBlock) > INT32_MAX) return ATTN_ERR_SHAPE;
+  if ((int64_t)Nq * d * 2 > INT32_MAX || (int64_t)Nk * d * 2 > INT32_MAX)
+    return ATTN_ERR_SHAPE;  // one head's bytes fit an int
+  if (bh * Nq > (int64_t)INT32_MAX * 32) return ATTN_ERR_SHAPE;  // delta grid
+  if (bh == 0 || (Nq == 0 && Nk == 0)) {
+    *nothing = true;
+    return ATTN_OK;
+  }
+  // Query-side buffers are unread when Nq = 0, key-side ones when Nk = 0.
+  if (Nq > 0 && (!q || !o || !lse || !dout || !dq || !delta)) return ATTN_ERR_NULL;
+  if (Nk > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_NULL;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, delta};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_ALIGN;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+  if (!device_is_gfx950(dev)) return ATTN_ERR_DEVICE;
+  return ATTN_OK;
+}
+
+template <bool GENERAL>
+int dispatch(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, float* delta, int BH, int Nq, int Nk,
+             int d, int causal, float scale, hipStream_t s) {
+  if (d == 64) {
+    return causal ? launch<64, true, GENERAL>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, Nq, Nk, scale, s)
+                  : launch<64, false, GENERAL>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, Nq, Nk, scale, s);
+  }
+  return causal ? launch<128, true, GENERAL>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, Nq, Nk, scale, s)
+                : launch<128, false, GENERAL>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, Nq, Nk, scale, s);
 }
 
 }  // namespace
@@ -592,30 +665,22 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
                         float* delta, int B, int H, int N, int d, int causal, float scale,
                         void* stream) {
-  if (B < 0 || H < 0 || N < 0) return ATTN_ERR_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
-  if (!(scale > 0.0f) || !isfinite(scale)) return ATTN_ERR_SCALE;
-  const int64_t bh = (int64_t)B * H;
-  if (bh > INT32_MAX) return ATTN_ERR_SHAPE;
-  if (2 * bh * (((int64_t)N + kBlock - 1) / kBlock) > INT32_MAX) return ATTN_ERR_SHAPE;  // grid
-  if ((int64_t)N * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;  // one head's bytes fit an int
-  if (bh * N > (int64_t)INT32_MAX * 32) return ATTN_ERR_SHAPE;  // delta grid
-  if (bh == 0 || N == 0) return ATTN_OK;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL;
-  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, delta};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return ATTN_ERR_ALIGN;
+  bool nothing = false;
+  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, N, d, scale, &nothing);
+  if (st != ATTN_OK || nothing) return st;
+  return dispatch<false>(q, k, v, o, lse, dout, dq, dk, dv, delta, B * H, N, N, d, causal, scale,
+                         static_cast<hipStream_t>(stream));
+}
 
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
-  if (!device_is_gfx950(dev)) return ATTN_ERR_DEVICE;
-
+extern "C" int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           float* delta, int B, int H, int Nq, int Nk, int d, int causal,
+                           float scale, void* stream) {
+  bool nothing = false;
+  const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, d, scale, &nothing);
+  if (st != ATTN_OK || nothing) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int BH = static_cast<int>(bh);
-  if (d == 64) {
-    return causal ? launch<64, true>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, scale, s)
-                  : launch<64, false>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, scale, s);
-  }
-  return causal ? launch<128, true>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, scale, s)
-                : launch<128, false>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, N, scale, s);
+  if (Nq == Nk)
+    return dispatch<false>(q, k, v, o, lse, dout, dq, dk, dv, delta, B * H, Nq, Nk, d, causal, scale, s);
+  return dispatch<true>(q, k, v, o, lse, dout, dq, dk, dv, delta, B * H, Nq, Nk, d, causal, scale, s);
 }

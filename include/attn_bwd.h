@@ -58,6 +58,28 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o,
              int causal, float scale,
              void *stream);
 
+/*
+ * attn_bwd_ex -- the same backward for Nq queries against Nk keys per head,
+ * the derivative of attn_fwd_ex (attn_fwd.h): causal masks are aligned
+ * bottom-right (key j visible to query i iff j <= i + Nk - Nq).
+ *
+ *   q, o, dout, dq   [B, H, Nq, d];   k, v, dk, dv   [B, H, Nk, d];
+ *   lse, delta       [B, H, Nq]       (lse from attn_fwd_ex on the same
+ *                                      problem; -inf for rows that see no key)
+ *
+ * A query row that sees no key gets dq = 0 and delta = 0 and adds nothing to
+ * dk or dv; with Nq = 0, dk = dv = 0.  Query-side pointers (q, o, lse, dout,
+ * dq, delta) may be NULL when Nq = 0 and key-side ones (k, v, dk, dv) when
+ * Nk = 0.  Every other argument, and ownership, errors and semantics, are as
+ * for attn_bwd; with Nq = Nk the call is exactly attn_bwd.
+ */
+int attn_bwd_ex(const void *q, const void *k, const void *v, const void *o,
+                const float *lse, const void *dout,
+                void *dq, void *dk, void *dv, float *delta,
+                int B, int H, int Nq, int Nk, int d,
+                int causal, float scale,
+                void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,7 +39,7 @@ def declared_functions():
 
 def test_headers_declare_the_entry_points():
     assert [os.path.basename(h) for h in HEADERS] == ["attn_bwd.h", "attn_fwd.h", "attn_gemm.h"]
-    assert declared_functions() == ["attn_bwd", "attn_fwd", "attn_fwd_abi_version",
+    assert declared_functions() == ["attn_bwd", "attn_bwd_ex", "attn_fwd", "attn_fwd_abi_version",
                                     "attn_fwd_ex", "attn_fwd_splitkv", "attn_fwd_strerror",
                                     "attn_gemm_bf16"]
 
@@ -276,3 +276,31 @@ def test_python_gemm_binding_rejects_bad_input():
         af.gemm(x, x)  # CPU tensors
     with pytest.raises(TypeError):
         af.gemm(x.float(), x)
+
+
+def call_bwd_ex(B=2, H=3, Nq=100, Nk=300, d=128, causal=1, scale=0.088, **ptrs):
+    names = ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta")
+    p = [ptrs.get(n, FAKE) for n in names]
+    return af.attn_bwd_ex_raw(*p, B, H, Nq, Nk, d, causal, scale)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Nq=-1), af.Status.ERR_SHAPE),
+    (dict(Nk=-1), af.Status.ERR_SHAPE),
+    (dict(d=96), af.Status.ERR_HEAD_DIM),
+    (dict(scale=0.0), af.Status.ERR_SCALE),
+    (dict(Nk=1 << 24), af.Status.ERR_SHAPE),
+    (dict(Nq=1 << 24), af.Status.ERR_SHAPE),
+] + [(dict(**{n: 0}), af.Status.ERR_NULL)
+     for n in ("q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta")]
+  + [(dict(**{n: FAKE + 4}), af.Status.ERR_ALIGN) for n in ("q", "dk", "delta")]
+  + [(dict(Nq=0, k=0), af.Status.ERR_NULL), (dict(Nk=0, q=0), af.Status.ERR_NULL)])
+def test_bwd_ex_rejects(lib, kw, status):
+    assert call_bwd_ex(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Nq=0, Nk=0),
+                                dict(Nq=0, Nk=0, q=0, k=0, v=0, o=0, lse=0, dout=0, dq=0, dk=0, dv=0,
+                                     delta=0)])
+def test_bwd_ex_empty_problem_is_a_noop(lib, kw):
+    assert call_bwd_ex(**kw) == af.Status.OK
