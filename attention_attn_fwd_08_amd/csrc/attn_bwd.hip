@@ -51,12 +51,11 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 template <int D>
 struct Geo {
+  static_assert(D == 32 || D == 64 || D == 96 || D == 128, "unsupported head dim");
   static constexpr int kRowBytes = D * 2;
   static constexpr int kSteps = D / 16;    // MFMA k-steps over the head dimension
   static constexpr int kDBlocks = D / 32;  // 32-row blocks of a transposed accumulator
   static constexpr int kTileBytes = kTile * kRowBytes;
-  static constexpr int kRowsPerLoad = kWave * 16 / kRowBytes;        // rows one wave copy fills
-  static constexpr int kLoads = kTile / (kRowsPerLoad * kWaves);     // copies per wave per tile
 };
 
 // Chunk swizzle for a tile read both ways.  A row read (16 lanes read one
@@ -64,11 +63,15 @@ struct Geo {
 // bank groups; a transposed read (32 lanes read 4 rows x 4 adjacent chunks)
 // needs those 16 (row, chunk) pairs distinct.  d=128 (256-byte rows):
 // 4*(row%4) + 2*(row/4 %2) + (row/8 %2).  d=64 (128-byte rows, two per bank
-// sweep): 4*(row/2 %2) + (row/4 %4).
+// sweep): 4*(row/2 %2) + (row/4 %4).  d=32 and d=96 (rows of 4 and 12
+// chunks: rows r, r+4, r+8, r+12 share a bank group, the residues of r mod 4
+// use disjoint ones, and the 4 rows of a transposed read already fall in 4
+// distinct bank quarters): (row/4 %4), which keeps a chunk in its group of 4.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (D == 128) return 4 * (row & 3) + 2 * ((row >> 2) & 1) + ((row >> 3) & 1);
-  else return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+  else if constexpr (D == 64) return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+  else return (row >> 2) & 3;
 }
 
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
@@ -99,18 +102,23 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 
 // Copy rows [row0, row0 + ROWS) of a [N, D] bf16 matrix into a swizzled LDS
 // tile (rows past N read as zeros).  Every wave copies its share of slices.
+// The tile is a row-major array of 16-byte chunks: lane i of wave copy w fills
+// chunk g = 64w + i (row g / chunks-per-row, physical chunk g % chunks-per-row,
+// holding the logical chunk physical ^ swz(row)).
 template <int D, int ROWS = kTile>
 __device__ __forceinline__ void copy_tile(const __bf16* mat, int N, int row0, unsigned tile_lds,
                                           int wave, int lane) {
   using G = Geo<D>;
   constexpr int kChunks = D / 8;
-  constexpr int kLoads = ROWS / (G::kRowsPerLoad * kWaves);
+  constexpr int kLoads = ROWS * kChunks / (kWave * kWaves);
+  static_assert(ROWS * kChunks % (kWave * kWaves) == 0, "tile must split evenly over the waves");
   const i32x4 rsrc = make_rsrc(mat + (size_t)row0 * D, (N - row0) * G::kRowBytes);
 #pragma unroll
   for (int it = 0; it < kLoads; ++it) {
-    const int r = (wave * kLoads + it) * G::kRowsPerLoad + lane / kChunks;
-    const int voff = r * G::kRowBytes + (((lane % kChunks) ^ swz<D>(r)) << 4);
-    load16_to_lds(rsrc, voff, tile_lds + (wave * kLoads + it) * G::kRowsPerLoad * G::kRowBytes);
+    const unsigned g = (wave * kLoads + it) * kWave + lane;
+    const int r = (int)(g / kChunks);
+    const int voff = r * G::kRowBytes + ((((int)(g % kChunks)) ^ swz<D>(r)) << 4);
+    load16_to_lds(rsrc, voff, tile_lds + (wave * kLoads + it) * kWave * 16);
   }
 }
 
@@ -170,18 +178,18 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const __bf16* __restrict__ o,
                                                         const __bf16* __restrict__ dout,
                                                         float* __restrict__ delta, long long rows) {
-  constexpr int kPer = D / 8;  // elements per lane: 16 (d=128) or 8 (d=64)
+  constexpr int kPer = D / 8;  // elements per lane (4, 8, 12 or 16)
   const long long row = (long long)blockIdx.x * 32 + threadIdx.x / 8;
   const int sub = threadIdx.x & 7;
   float acc = 0.f;
   if (row < rows) {
-    const bf16x8* po = reinterpret_cast<const bf16x8*>(o + row * D + sub * kPer);
-    const bf16x8* pg = reinterpret_cast<const bf16x8*>(dout + row * D + sub * kPer);
+    const bf16x4* po = reinterpret_cast<const bf16x4*>(o + row * D + sub * kPer);
+    const bf16x4* pg = reinterpret_cast<const bf16x4*>(dout + row * D + sub * kPer);
 #pragma unroll
-    for (int c = 0; c < kPer / 8; ++c) {
-      const bf16x8 a = po[c], g = pg[c];
+    for (int c = 0; c < kPer / 4; ++c) {
+      const bf16x4 a = po[c], g = pg[c];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc = fmaf((float)a[j], (float)g[j], acc);
+      for (int j = 0; j < 4; ++j) acc = fmaf((float)a[j], (float)g[j], acc);
     }
   }
   acc += __shfl_xor(acc, 1, 8);
@@ -388,7 +396,7 @@ __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __
   }
 }
 
-// d=64: dK and dV in one workgroup per key block.
+// d=32, 64 and 96: dK and dV in one workgroup per key block.
 template <int D, bool CAUSAL, bool GENERAL>
 __global__ __launch_bounds__(kWaves * kWave, 2)
 void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
@@ -622,7 +630,7 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
               int B, int H, int Nq, int Nk, int d, float scale, bool* nothing) {
   *nothing = false;
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (d != 32 && d != 64 && d != 96 && d != 128) return ATTN_ERR_HEAD_DIM;
   if (!(scale > 0.0f) || !isfinite(scale)) return ATTN_ERR_SCALE;
   const int64_t bh = (int64_t)B * H;
   if (bh > INT32_MAX) return ATTN_ERR_SHAPE;
@@ -651,12 +659,17 @@ template <bool GENERAL>
 int dispatch(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dout, void* dq, void* dk, void* dv, float* delta, int BH, int Nq, int Nk,
              int d, int causal, float scale, hipStream_t s) {
-  if (d == 64) {
-    return causal ? launch<64, true, GENERAL>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, Nq, Nk, scale, s)
-                  : launch<64, false, GENERAL>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, Nq, Nk, scale, s);
+  auto go = [&](auto d_tag) {
+    constexpr int D = decltype(d_tag)::value;
+    return causal ? launch<D, true, GENERAL>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, Nq, Nk, scale, s)
+                  : launch<D, false, GENERAL>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, Nq, Nk, scale, s);
+  };
+  switch (d) {
+    case 32: return go(std::integral_constant<int, 32>{});
+    case 64: return go(std::integral_constant<int, 64>{});
+    case 96: return go(std::integral_constant<int, 96>{});
+    default: return go(std::integral_constant<int, 128>{});
   }
-  return causal ? launch<128, true, GENERAL>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, Nq, Nk, scale, s)
-                : launch<128, false, GENERAL>(q, k, v, o, lse, dout, dq, dk, dv, delta, BH, Nq, Nk, scale, s);
 }
 
 }  // namespace

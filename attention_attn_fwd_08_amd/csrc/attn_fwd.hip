@@ -798,7 +798,7 @@ extern "C" const char* attn_fwd_strerror(int status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "B, H or N is negative, or the problem size overflows";
-    case ATTN_ERR_HEAD_DIM: return "head dimension d must be 32, 64, 96, 128 or 256 (backward: 64 or 128)";
+    case ATTN_ERR_HEAD_DIM: return "head dimension d must be 32, 64, 96, 128 or 256 (backward: 32, 64, 96 or 128)";
     case ATTN_ERR_SEQ_MULTIPLE: return "reserved (any sequence length is accepted)";
     case ATTN_ERR_ALIGN: return "q, k, v, o and lse must be 16-byte aligned";
     case ATTN_ERR_SCALE: return "scale must be finite and greater than 0";

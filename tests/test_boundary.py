@@ -146,7 +146,7 @@ def call_bwd(B=2, H=3, N=256, d=128, causal=0, scale=0.088, **ptrs):
 @pytest.mark.parametrize("kw,status", [
     (dict(B=-1), af.Status.ERR_SHAPE),
     (dict(N=-1), af.Status.ERR_SHAPE),
-    (dict(d=32), af.Status.ERR_HEAD_DIM),
+    (dict(d=48), af.Status.ERR_HEAD_DIM),
     (dict(d=256), af.Status.ERR_HEAD_DIM),
     (dict(scale=0.0), af.Status.ERR_SCALE),
     (dict(scale=float("nan")), af.Status.ERR_SCALE),
@@ -287,7 +287,7 @@ def call_bwd_ex(B=2, H=3, Nq=100, Nk=300, d=128, causal=1, scale=0.088, **ptrs):
 @pytest.mark.parametrize("kw,status", [
     (dict(Nq=-1), af.Status.ERR_SHAPE),
     (dict(Nk=-1), af.Status.ERR_SHAPE),
-    (dict(d=96), af.Status.ERR_HEAD_DIM),
+    (dict(d=256), af.Status.ERR_HEAD_DIM),
     (dict(scale=0.0), af.Status.ERR_SCALE),
     (dict(Nk=1 << 24), af.Status.ERR_SHAPE),
     (dict(Nq=1 << 24), af.Status.ERR_SHAPE),

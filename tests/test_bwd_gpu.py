@@ -55,7 +55,7 @@ def check_delta(delta, o, g, what):
 
 
 SHAPES = [
-    # (B, H, N, d, causal): several tiles, ragged tails, both head dims
+    # (B, H, N, d, causal): several tiles, ragged tails, every head dim
     (1, 2, 256, 64, False), (1, 2, 256, 64, True),
     (1, 2, 256, 128, False), (1, 2, 256, 128, True),
     (2, 1, 640, 128, True), (1, 3, 1024, 64, True),
@@ -63,6 +63,7 @@ SHAPES = [
     (1, 2, 1, 128, True), (1, 2, 1, 64, False),
     (1, 1, 31, 64, True), (1, 1, 33, 128, True),
     (2, 1, 200, 128, True), (1, 2, 333, 64, False), (1, 1, 1000, 128, True),
+    (1, 2, 256, 32, False), (2, 1, 333, 32, True), (1, 2, 256, 96, True), (1, 1, 700, 96, False),
 ]
 
 
