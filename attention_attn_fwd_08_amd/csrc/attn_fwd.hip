@@ -8,9 +8,11 @@
 // and normaliser l so the N x N matrix never exists.
 //
 // Mapping to CDNA4 (not to the examples' warp/warpgroup design):
-//   * a workgroup is 4 waves of 64 lanes owning 128 queries (32 per wave), and
-//     each SIMD runs two such waves (two workgroups per CU): the MFMA pipe
-//     of one wave overlaps the softmax VALU work of the other;
+//   * each wave of 64 lanes owns 32 queries; at d=128 a workgroup is 8 waves
+//     (256 queries, one workgroup per CU), at the other head dims 4 waves
+//     (128 queries, two or more per CU; one at d=256).  Two waves share each
+//     SIMD, so the MFMA pipe of one overlaps the softmax VALU work of the
+//     other (d=256: one wave per SIMD, with the O accumulator in AGPRs);
 //   * scores are formed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: K (from LDS) is the A operand, Q^T (held in
 //     registers for the whole workgroup) the B operand.  In the 32x32
@@ -33,9 +35,13 @@
 //     directly (no register staging), double-buffered, with XOR swizzles
 //     that make every operand read bank-conflict free;
 //   * causal: key tiles past the workgroup's last query are never loaded,
-//     and only the two tiles on the workgroup's diagonal are masked;
+//     and only the tiles on the workgroup's diagonal are masked;
 //   * any N: a partial last query tile reads clamped Q rows and stores only
 //     rows < N; keys >= N read as zeros and are masked in the last key tile;
+//   * general shapes (Nq queries against Nk keys, bottom-right causal mask)
+//     and split-KV (key ranges in separate workgroups, fp32 partial results
+//     merged by log-sum-exp in attn_merge_kernel) are instances of the same
+//     kernel; waves whose queries all lie past Nq only copy and wait;
 //   * workgroup ids are remapped so that tiles of one head run on one XCD
 //     (workgroups are dispatched round-robin over the 8 XCDs), keeping that
 //     head's K/V in the XCD's L2; causal tiles of a head run longest first.
