@@ -24,13 +24,15 @@
 //     order inside each 16-key step is permuted the same way in V^T (read with
 //     ds_read_b64_tr_b16), which the contraction does not see;
 //   * softmax uses exp2 with log2(e) folded into the scale: p = 2^(s*c - m*c)
-//     with c = scale*log2(e), and lse = (m*c + log2 l) * ln 2.  O is rescaled
-//     only when a running maximum grows by more than 2^8 (rare after the
-//     first tile), otherwise the stale reference maximum is kept;
+//     with c = scale*log2(e), and lse = (m*c + log2 l) * ln 2.  The
+//     reference maximum m is the first tile's; later tiles are not reduced
+//     to their maxima.  O is rescaled only when a tile's probabilities against
+//     the stale m grow past 2^64 (seen in the lane's tile sum), which ordinary
+//     scores never reach after the first tile;
 //   * the 64-key tile loop is software pipelined: while the scores of tile t
 //     become probabilities (VALU) the MFMA pipe computes the scores of tile
-//     t+1, and while O^T += V_t^T P_t^T runs the VALU reduces tile t+1 to its
-//     row maxima; K therefore runs one tile ahead of V;
+//     t+1, and O^T += V_t^T P_t^T follows on the MFMA pipe; K therefore runs
+//     one tile ahead of V;
 //   * K and V tiles stream global -> LDS with buffer loads that write LDS
 //     directly (no register staging), double-buffered, with XOR swizzles
 //     that make every operand read bank-conflict free;
@@ -84,10 +86,13 @@ struct Launch {
 };
 constexpr int kBlockN = 64;                        // keys per LDS stage
 constexpr int kXcds = 8;
-// O is rescaled only when a query's block maximum exceeds the reference
-// maximum by more than this many powers of two; until then probabilities are
-// formed against the stale reference (they stay <= 2^8, exact to rescale).
-constexpr float kRescaleLog2 = 8.0f;
+// Probabilities are formed against a stale reference maximum for as long as
+// a lane's sum over one tile stays at or below this (2^64): each is then at
+// most 2^64, which bf16 and the fp32 accumulators hold with their usual
+// relative precision (and far from overflow).  Beyond it (or NaN / inf), the
+// tile's exact maximum becomes the reference, O and l are rescaled, and the
+// tile's probabilities are formed again.
+constexpr float kProbSumCap = 18446744073709551616.0f;
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -444,8 +449,8 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
   }
 
-  // Prologue: scores of tile 0 and the first reference maximum.  Tile 0
-  // holds key 0, which every query sees, so the maximum is finite.
+  // Prologue: scores of tile 0 and the reference maximum, tile 0's (finite
+  // for every query in the square case, where tile 0 holds key 0).
   f32x16 s_a[2], s_b[2];
   scores<D>(k_base, k_off, qf, s_a);
   if (first_mask == 0) mask_tile<CAUSAL>(s_a, 0, q0 + off, Nk, l32, half);
@@ -491,24 +496,49 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       }
     }
     // A row that has seen no key yet has m_ref = -inf and only -inf scores.
-    const float mc = (GENERAL && m_ref == -INFINITY) ? 0.f : m_ref * c;
+    float mc = (GENERAL && m_ref == -INFINITY) ? 0.f : m_ref * c;
     bf16x8 pb[2][2];
+    float l_tile = 0.f;
+    auto probs = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      if (CHECK && !live(t, sb)) continue;  // its probabilities are all 0
+      for (int sb = 0; sb < 2; ++sb) {
+        if (CHECK && !live(t, sb)) continue;  // its probabilities are all 0
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        float p[8];
+        for (int cc = 0; cc < 2; ++cc) {
+          float p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(fmaf(s_cur[sb][8 * cc + j], c, -mc));
-          pb[sb][cc][j] = (__bf16)p[j];
+          for (int j = 0; j < 8; ++j) {
+            p[j] = __builtin_amdgcn_exp2f(fmaf(s_cur[sb][8 * cc + j], c, -mc));
+            pb[sb][cc][j] = (__bf16)p[j];
+          }
+          l_tile += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         }
-        l_run += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       }
+    };
+    probs();
+    // Lazy rescale, checked on the probabilities themselves (the lane's tile
+    // sum; NaN and inf fail the test too).  Rare: the tile's exact maximum
+    // becomes the reference (lanes L and L^32 agree on it), O and l are
+    // rescaled and the probabilities formed again.  A row that has seen no
+    // key until now (m = -inf, general shapes) takes its first finite m here.
+    bool redo = !(l_tile <= kProbSumCap);
+    if constexpr (GENERAL) redo = redo || (m_ref == -INFINITY && l_tile > 0.f);
+    if (__builtin_amdgcn_ballot_w64(redo)) {
+      const float m_new = fmaxf(m_ref, tile_max(s_cur));
+      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < kDBlocks; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
+      m_ref = m_new;
+      mc = (GENERAL && m_ref == -INFINITY) ? 0.f : m_ref * c;
+      l_tile = 0.f;
+      probs();
     }
+    l_run += l_tile;
 
-    // Phase B: O^T += V_t^T P_t^T on MFMA while the VALU reduces S_{t+1}.
+    // Phase B: O^T += V_t^T P_t^T on MFMA (and the mask of tile t+1 when it needs one).
     const unsigned char* const v_lds = v_base + (t & 1) * kStageBytes;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
@@ -526,19 +556,6 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     }
     if constexpr (HAS_NEXT) {
       if constexpr (MASK_NEXT) mask_tile<CAUSAL>(s_next, (t + 1) * kBlockN, q0 + off, Nk, l32, half);
-      const float mx = tile_max(s_next);
-      // Lazy rescale: lanes L and L^32 agree on mx and m_ref, hence on `grow`.
-      const bool grow = (mx - m_ref) * c > kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform and rare
-        const float m_new = grow ? mx : m_ref;
-        const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c);
-        l_run *= alpha;
-#pragma unroll
-        for (int b = 0; b < kDBlocks; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
-        m_ref = m_new;
-      }
     }
   };
   using yes = std::true_type;
