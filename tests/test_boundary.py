@@ -228,9 +228,14 @@ def test_splitkv_empty_problem_is_a_noop(lib, kw):
 
 
 def test_splitkv_split_choice():
-    assert af.splitkv_splits(1, 8, 1, 65536, 128) == 64
+    """One round of workgroups: 256 at d=128 (one per CU), 512 at d=64."""
+    assert af.splitkv_splits(1, 8, 1, 65536, 128) == 32
+    assert af.splitkv_splits(1, 32, 1, 65536, 128) == 8
+    assert af.splitkv_splits(4, 32, 1, 16384, 128) == 2
+    assert af.splitkv_splits(1, 32, 1, 65536, 64) == 16
     assert af.splitkv_splits(16, 16, 4096, 4096, 128) == 1
     assert af.splitkv_splits(1, 1, 1, 100, 64) == 1
+    assert af.splitkv_splits(1, 1, 1, 1000, 128) == 3  # at least 256 keys per split
 
 
 def call_gemm(M=300, N=264, K=200, layout=0, a=FAKE, b=FAKE, c=FAKE):
