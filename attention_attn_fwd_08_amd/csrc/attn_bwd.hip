@@ -286,20 +286,34 @@ __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __
   const int qt_first = CAUSAL ? max(kb * kBlock - off, 0) / kQT : 0;
   const int n_qt = (Nq + kQT - 1) / kQT;
   auto stage_ptr = [&](int s) __attribute__((always_inline)) { return smem + s * kStageBytes; };
+  // The stage's lse slot holds lse * log2(e) (0 past Nq): wave 0 reads the 64
+  // values with ordinary loads when it issues the tile and writes the
+  // products before the barrier that publishes the tile, so the exponent of
+  // P below is one fma.
+  static_assert(kQT == kWave, "one lse value per lane of wave 0");
+  float lse_next = 0.f;
   auto issue = [&](int qt, int s) __attribute__((always_inline)) {
     unsigned char* st_base = stage_ptr(s);
     const int row0 = qt * kQT;
     copy_tile<D, kQT>(qh, Nq, row0, lds_addr(st_base), wave, lane);
     copy_tile<D, kQT>(doh, Nq, row0, lds_addr(st_base + kTileBytes), wave, lane);
     if (wave == 0) {
-      copy_vec<kQT>(lseh, Nq, row0, lds_addr(st_base + 2 * kTileBytes), lane);
       copy_vec<kQT>(dlth, Nq, row0, lds_addr(st_base + 2 * kTileBytes + kQT * 4), lane);
+      lse_next = row0 + lane < Nq ? lseh[row0 + lane] : 0.f;
     }
   };
-  if (qt_first < n_qt) issue(qt_first, 0);
+  auto publish_lse = [&](int s) __attribute__((always_inline)) {
+    if (wave == 0) reinterpret_cast<float*>(stage_ptr(s) + 2 * kTileBytes)[lane] = lse_next * kLog2e;
+  };
+  if (qt_first < n_qt) {
+    issue(qt_first, 0);
+    publish_lse(0);
+  }
 
-  for (int qt = qt_first; qt < n_qt; ++qt) {
-    const int s = (qt - qt_first) & 1;
+  // One Q/dO tile; the stage is a compile-time constant, so every LDS read
+  // is a lane offset plus an immediate.
+  auto tile = [&](auto stage_tag, int qt) __attribute__((always_inline)) {
+    constexpr int s = decltype(stage_tag)::value;
     wait_lds_dma_all();
     __syncthreads();  // tile qt has landed; the other stage is free
     if (qt + 1 < n_qt) issue(qt + 1, s ^ 1);
@@ -334,7 +348,7 @@ __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = 4 * g + j;
-          float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -l4[j] * kLog2e));
+          float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -l4[j]));
           if constexpr (MASK) {  // (a row that sees no key has lse = -inf: p is selected away)
             const int query = qt * kQT + qi + j;
             const bool vis = CAUSAL ? (key0 + l32 <= query + off && query < Nq) : (query < Nq);
@@ -372,6 +386,11 @@ __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __
       else soft(std::true_type{}, qb, sacc, pacc, pb, sb);
       pv(qb, pb, sb);
     }
+    if (qt + 1 < n_qt) publish_lse(s ^ 1);
+  };
+  for (int qt = qt_first; qt < n_qt; qt += 2) {
+    tile(std::integral_constant<int, 0>{}, qt);
+    if (qt + 1 < n_qt) tile(std::integral_constant<int, 1>{}, qt + 1);
   }
 
   // Epilogue: lane = key; registers 4j..4j+3 of block b are features
@@ -508,19 +527,19 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   };
   if (n_kt > 0) issue(0, 0);
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int s = kt & 1;
+  // One K/V tile; the stage is a compile-time constant, so every LDS read is
+  // a lane offset plus an immediate.
+  auto tile = [&](auto stage_tag, int kt) __attribute__((always_inline)) {
+    constexpr int s = decltype(stage_tag)::value;
     wait_lds_dma_all();
     __syncthreads();  // tile kt has landed; the other stage is free
     if (kt + 1 < n_kt) issue(kt + 1, s ^ 1);
     const unsigned char* const k_lds = smem + s * kStageBytes;
     const unsigned char* const v_lds = k_lds + kTileBytes;
-    const bool partial =
-        kt * kTile + kTile - 1 > wave_last_key || (CAUSAL && kt * kTile + kTile - 1 > q0 + off);
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+    // One 32-key block; with MASK, keys past Nk or above the diagonal get P = 0.
+    auto block = [&](auto mask_tag, int sb) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
       const int key0 = kt * kTile + sb * kRows;
-      if (key0 > wave_last_key) continue;  // no query of this wave sees the block
       const unsigned char* const ka = k_lds + sb * kRows * G::kRowBytes;
       const unsigned char* const va = v_lds + sb * kRows * G::kRowBytes;
       // S^T = K Q^T and dP^T = V dO^T: [keys, queries]; lane = query,
@@ -537,7 +556,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -lse2));
-        if (partial) {
+        if constexpr (MASK) {
           const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
           const bool vis = key < Nk && (!CAUSAL || key <= query + off);
           p = vis ? p : 0.f;
@@ -550,7 +569,21 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
         for (int b = 0; b < kDBlocks; ++b)
           dqt[b] = mfma(read_tr(ka, tro[cc][b][0], tro[cc][b][1]), sbf[cc], dqt[b]);
+    };
+    const bool partial =
+        kt * kTile + kTile - 1 > wave_last_key || (CAUSAL && kt * kTile + kTile - 1 > q0 + off);
+    if (partial) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)  // a block past the wave's last visible key is skipped
+        if (kt * kTile + sb * kRows <= wave_last_key) block(std::true_type{}, sb);
+    } else {
+      block(std::false_type{}, 0);
+      block(std::false_type{}, 1);
     }
+  };
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    tile(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < n_kt) tile(std::integral_constant<int, 1>{}, kt + 1);
   }
 
   if (query < Nq) {
