@@ -182,9 +182,9 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 // Per-wave state and the steps of one 64-key tile.  The tile loop is software
 // pipelined: while the scores of tile t are turned into probabilities (VALU,
-// transcendental) the MFMA pipe computes the scores of tile t+1, and while
-// O^T += V_t^T P_t^T runs on the MFMA pipe the VALU reduces tile t+1's
-// scores to their row maximum.  K therefore runs one tile ahead of V.
+// transcendental) the MFMA pipe computes the scores of tile t+1, and then
+// O^T += V_t^T P_t^T runs on the MFMA pipe (with the mask of tile t+1 on the
+// VALU when it needs one).  K therefore runs one tile ahead of V.
 template <int D>
 struct Tile {
   static constexpr int kRowBytes = D * 2;
