@@ -479,6 +479,10 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     if (HAS_NEXT) load_v(t + 1, (t + 1) & 1);
 
     // Phase A: probabilities of tile t (VALU) while S_{t+1} runs on MFMA.
+    // The wave runs this phase at raised issue priority: where the two waves
+    // of a SIMD contend, the one interleaving score MFMAs with the softmax
+    // goes first (measured 2-3 % faster than equal priorities).
+    __builtin_amdgcn_s_setprio(1);
     if constexpr (HAS_NEXT) {
       const unsigned char* const k_lds = k_base + ((t + 1) & 1) * kStageBytes;
       if constexpr (CHECK) {
@@ -537,6 +541,8 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       probs();
     }
     l_run += l_tile;
+
+    __builtin_amdgcn_s_setprio(0);
 
     // Phase B: O^T += V_t^T P_t^T on MFMA (and the mask of tile t+1 when it needs one).
     const unsigned char* const v_lds = v_base + (t & 1) * kStageBytes;
