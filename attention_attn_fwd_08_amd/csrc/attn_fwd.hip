@@ -155,13 +155,25 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
 }
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// The LDS address is `lds_addr + OFF`, OFF a compile-time byte offset added
+// inside the asm, so only the base occupies a scalar register.
+template <unsigned OFF>
 __device__ __forceinline__ void load16_to_lds(i32x4 rsrc, int voff, unsigned lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "s"(lds_addr)
-               : "memory", "m0");
+               : "v"(voff), "s"(rsrc), "s"(lds_addr), "n"(OFF)
+               : "memory", "m0", "scc");
 }
 #pragma clang diagnostic pop
+// f(integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Wait until at most N of this wave's LDS-bound loads are still in flight.
 template <int N>
 __device__ __forceinline__ void wait_lds_dma() {
@@ -234,7 +246,11 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int key0, int q0, int 
   const int last = CAUSAL ? min(q0 + l32, N - 1) : N - 1;  // last visible key
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb) {
-    const int lim = last - key0 - sb * 32 - 4 * half;  // visible iff in-block offset <= lim
+    int lim = last - key0 - sb * 32 - 4 * half;  // visible iff in-block offset <= lim
+    // Opaque to the optimiser: the 16 lane masks below are then formed where
+    // they are used, not hoisted out of the tile loops, where they would hold
+    // 32 scalar register pairs across the whole loop.
+    asm volatile("" : "+v"(lim));
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       if (8 * (r >> 2) + (r & 3) > lim) s[sb][r] = -INFINITY;
@@ -259,14 +275,20 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
 // blockIdx.y takes only keys [y*kv_chunk, (y+1)*kv_chunk) and writes its
 // normalised partial O (fp32) and partial lse to o_part / lse_part, laid out
 // [split, head, query, d] and [split, head, query]; a merge kernel combines
-// the splits.
-template <int D, bool CAUSAL, bool GENERAL, bool SPLIT = false>
+// the splits.  PERSIST (square shapes only): the grid is one workgroup per
+// resident slot and each workgroup walks n_work query tiles' worth of
+// logical ids; the next tile's K/V/Q loads are issued before the current
+// tile's output is stored, so a tile's start-up overlaps the previous
+// tile's epilogue instead of leaving the CU idle between workgroups.
+template <int D, bool CAUSAL, bool GENERAL, bool SPLIT = false, bool PERSIST = false>
 __global__ __launch_bounds__(Launch<D>::kThreads, Launch<D>::kMinBlocks)  // <= 256 registers
 void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, __bf16* __restrict__ o,
                      float* __restrict__ lse, int N, float c, int nk_arg, int off_arg,
-                     int kv_chunk, float* __restrict__ o_part, float* __restrict__ lse_part) {
+                     int kv_chunk, float* __restrict__ o_part, float* __restrict__ lse_part,
+                     int n_work) {
   static_assert(!SPLIT || GENERAL, "a split is a general-shape problem");
+  static_assert(!PERSIST || !GENERAL, "the persistent walk is for square shapes");
   const int Nk_all = GENERAL ? nk_arg : N;
   const int kv_begin = SPLIT ? (int)blockIdx.y * kv_chunk : 0;  // first key of this split
   const int Nk = SPLIT ? min(kv_chunk, Nk_all - kv_begin) : Nk_all;
@@ -294,67 +316,34 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int l32 = lane & 31;
   const int half = lane >> 5;
 
-  // Workgroup -> (head, query tile).  Workgroups are dispatched round-robin
-  // over the XCDs; the remap gives each XCD a contiguous range of logical ids,
-  // and consecutive logical ids walk the query tiles of one head, so the
-  // workgroups resident on an XCD share one head's K/V in that XCD's L2.
-  // Causal tiles of a head run longest first, so each XCD ends on short ones.
+  // Workgroup -> logical ids -> (head, query tile).  Workgroups are
+  // dispatched round-robin over the XCDs; the remap gives each XCD a
+  // contiguous range of logical ids, and consecutive logical ids walk the
+  // query tiles of one head, so the workgroups resident on an XCD share one
+  // head's K/V in that XCD's L2.  Causal tiles of a head run longest first,
+  // so each XCD ends on short ones.  A persistent workgroup (slot j of the
+  // S = grid/8 on its XCD) takes, in round r, position j of the r-th run of
+  // S ids in its XCD's range; causal rounds alternate with position S-1-j, so
+  // a slot's long diagonal tiles pair with short ones.
   const int n_qt = (N + kBlockM - 1) / kBlockM;
   const int grid = gridDim.x;
   int lid = blockIdx.x;
-  if (grid % kXcds == 0) lid = (lid % kXcds) * (grid / kXcds) + lid / kXcds;
-  const int head = lid / n_qt;
-  const int qt = CAUSAL ? n_qt - 1 - lid % n_qt : lid % n_qt;
-
-  const size_t head_off = (size_t)head * N * D;
-  const size_t kv_head_off = ((size_t)head * Nk_all + kv_begin) * D;
-  // SPLIT: this row's slot in the partial results.
-  const size_t part_row0 = SPLIT ? ((size_t)blockIdx.y * (grid / n_qt) + head) * N : 0;
-  const __bf16* const qh = q + head_off;
-  const __bf16* const kh = k + kv_head_off;
-  const __bf16* const vh = v + kv_head_off;
-  const int q0 = qt * kBlockM + wave * kQueriesPerWave;  // this wave's first query
-
-  // Tiles this workgroup visits; tiles from first_mask on are masked:
-  // causal, the tiles on the diagonal of at least one of its waves; else
-  // only a last tile that runs past N.
-  const int kv_end = CAUSAL ? min((qt + 1) * kBlockM + off, Nk) : Nk;
-  const int n_tiles = (kv_end + kBlockN - 1) / kBlockN;
-  int first_mask;
-  if constexpr (!GENERAL) {
-    first_mask = CAUSAL ? qt * (kBlockM / kBlockN) : (N % kBlockN ? n_tiles - 1 : n_tiles);
-  } else if constexpr (CAUSAL) {
-    // Tiles wholly at or below the workgroup's first query (+ off) need no mask.
-    const int first_last_key = qt * kBlockM + off;  // last key its first query sees
-    first_mask = first_last_key < 0 ? 0 : min((first_last_key + 1) / kBlockN, n_tiles);
-    if (kv_end == Nk && Nk % kBlockN) first_mask = min(first_mask, n_tiles - 1);
-  } else {
-    first_mask = Nk % kBlockN ? n_tiles - 1 : n_tiles;
-  }
-  if constexpr (GENERAL) {
-    if (n_tiles <= 0) {  // no query of the workgroup sees a key
-      const int qrow = q0 + l32;
-      if (qrow < N) {
-        if constexpr (SPLIT) {
-          float* const prow = o_part + (part_row0 + qrow) * D;
-#pragma unroll
-          for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              *reinterpret_cast<f32x4*>(prow + 32 * b + 8 * j + 4 * half) = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (half == 0) lse_part[part_row0 + qrow] = -INFINITY;
-        } else {
-          __bf16* const orow = o + head_off + (size_t)qrow * D;
-#pragma unroll
-          for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * j + 4 * half) = bf16x4{0, 0, 0, 0};
-          if (half == 0) lse[(size_t)head * N + qrow] = -INFINITY;
-        }
-      }
-      return;
+  int lid_begin = 0, lid_end = n_work, slots = grid, slot = lid, round = 0;
+  auto lid_at = [&](int r) __attribute__((always_inline)) {
+    return lid_begin + r * slots + ((CAUSAL && (r & 1)) ? slots - 1 - slot : slot);
+  };
+  if constexpr (PERSIST) {
+    if (grid % kXcds == 0) {
+      const int per_xcd = (n_work + kXcds - 1) / kXcds;
+      lid_begin = (lid % kXcds) * per_xcd;
+      lid_end = min(n_work, lid_begin + per_xcd);
+      slots = grid / kXcds;
+      slot = lid / kXcds;
     }
+    lid = lid_at(0);
+    if (lid >= lid_end) return;  // no tile for this workgroup (uniform)
+  } else {
+    if (grid % kXcds == 0) lid = (lid % kXcds) * (grid / kXcds) + lid / kXcds;
   }
 
   // Global -> LDS copy of one K or V tile.  The stage is a row-major array of
@@ -373,34 +362,18 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
   const unsigned lds_wave = (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)smem +
                             wave * kLoadsPerWave * kLoadBytes;
-  auto load_tile = [&](const __bf16* base, const int (&ld_off)[kLoadsPerWave], int region,
+  auto load_tile = [&](const __bf16* base, const int (&ld_off)[kLoadsPerWave], auto region_tag,
                        int tile, int stage) __attribute__((always_inline)) {
+    constexpr unsigned kRegion = decltype(region_tag)::value * 2u * kStageBytes;
     const i32x4 rsrc = make_rsrc(base + (size_t)tile * kBlockN * D, (Nk - tile * kBlockN) * kRowBytes);
-    const unsigned dst = lds_wave + (2 * region + stage) * kStageBytes;
-#pragma unroll
-    for (int it = 0; it < kLoadsPerWave; ++it)
-      load16_to_lds(rsrc, ld_off[it], dst + it * kLoadBytes);
+    const unsigned dst = lds_wave + stage * kStageBytes;
+    static_for<0, kLoadsPerWave>([&](auto it_tag) __attribute__((always_inline)) {
+      constexpr int it = decltype(it_tag)::value;
+      load16_to_lds<kRegion + it * kLoadBytes>(rsrc, ld_off[it], dst);
+    });
   };
-  auto load_k = [&](int tile, int stage) __attribute__((always_inline)) {
-    load_tile(kh, k_ld_off, 0, tile, stage);
-  };
-  auto load_v = [&](int tile, int stage) __attribute__((always_inline)) {
-    load_tile(vh, v_ld_off, 1, tile, stage);
-  };
-
-  load_k(0, 0);
-  load_v(0, 0);
-  if (n_tiles > 1) load_k(1, 1);
-
-  // Q^T as MFMA B operand: lane L holds query q0+L%32, features 8*(L/32)..+7
-  // of each 16-feature step.  Loaded once per tile.
-  bf16x8 qf[kSteps];
-  {
-    const int row = min(q0 + l32, N - 1);  // rows past N: any valid row
-    const __bf16* qrow = qh + (size_t)row * D + 8 * half;
-#pragma unroll
-    for (int st = 0; st < kSteps; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st);
-  }
+  using kRegionK = std::integral_constant<int, 0>;
+  using kRegionV = std::integral_constant<int, 1>;
 
   // Per-lane LDS byte offsets (stage-relative) of the operand reads.
   // K (A operand of S^T): row L%32 (+32 per block), logical chunk 2*st + L/32.
@@ -425,201 +398,300 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     v_off[h] = r * kRowBytes + (((col >> 3) ^ v_swz<D>(r)) << 4) + (col & 7) * 2;
   }
 
-  f32x16 acc[kDBlocks];
-#pragma unroll
-  for (int b = 0; b < kDBlocks; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
-
-  wait_lds_dma<0>();
-  __syncthreads();  // K0, V0, K1 have landed
-
-  if constexpr (GENERAL) {
-    // A wave whose 32 queries all lie past the last query (a short query
-    // block, e.g. decoding) computes nothing; it still issues its share of
-    // the copies and meets every barrier the tile loop below does.
-    if (q0 >= N) {
-      for (int t = 0; t < n_tiles; ++t) {
-        wait_lds_dma<0>();
-        __syncthreads();
-        if (t + 2 < n_tiles) load_k(t + 2, t & 1);
-        if (t + 1 < n_tiles) load_v(t + 1, (t + 1) & 1);
-      }
-      return;
-    }
-  }
-
-  // Prologue: scores of tile 0 and the reference maximum, tile 0's (finite
-  // for every query in the square case, where tile 0 holds key 0).
-  f32x16 s_a[2], s_b[2];
-  scores<D>(k_base, k_off, qf, s_a);
-  if (first_mask == 0) mask_tile<CAUSAL>(s_a, 0, q0 + off, Nk, l32, half);
-  float m_ref = tile_max(s_a);  // reference maximum (raw score units), query q0+L%32
-  float l_run = 0.f;            // this lane's half of the normaliser
-
-  // One tile: s_cur holds tile t's (masked) scores, s_next receives tile
-  // t+1's.  HAS_NEXT and MASK_NEXT are compile-time so the body is straight
-  // line code the scheduler can interleave (MFMA of one phase against VALU).
-  // A 32-key block is live for this wave iff its first key is visible to at
-  // least one of the wave's queries; dead blocks (above the diagonal, or past
-  // N) skip their MFMAs and exponentials.  Only the steps that can meet one
-  // (masked successor, or the last tile) test this.
-  const int wave_last_key = CAUSAL ? min(q0 + kQueriesPerWave - 1 + off, Nk - 1) : Nk - 1;
-  auto live = [&](int tile, int sb) __attribute__((always_inline)) {
-    return tile * kBlockN + sb * 32 <= wave_last_key;
+  // Last key tile (exclusive) a query tile visits.
+  auto tiles_of = [&](int qt) __attribute__((always_inline)) {
+    const int kv_end = CAUSAL ? min((qt + 1) * kBlockM + off, Nk) : Nk;
+    return (kv_end + kBlockN - 1) / kBlockN;
   };
-  auto step = [&](auto has_next_tag, auto mask_next_tag, int t, f32x16(&s_cur)[2],
-                  f32x16(&s_next)[2]) __attribute__((always_inline)) {
-    constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
-    constexpr bool MASK_NEXT = decltype(mask_next_tag)::value;
-    constexpr bool CHECK = MASK_NEXT || !HAS_NEXT;  // may meet dead blocks
-    wait_lds_dma<0>();
-    __syncthreads();  // K_{t+1} and V_t have landed; K_t and V_{t-1} are free
-    if (t + 2 < n_tiles) load_k(t + 2, t & 1);
-    if (HAS_NEXT) load_v(t + 1, (t + 1) & 1);
-
-    // Phase A: probabilities of tile t (VALU) while S_{t+1} runs on MFMA.
-    // The wave runs this phase at raised issue priority: where the two waves
-    // of a SIMD contend, the one interleaving score MFMAs with the softmax
-    // goes first (measured 2-3 % faster than equal priorities).
-    __builtin_amdgcn_s_setprio(1);
-    if constexpr (HAS_NEXT) {
-      const unsigned char* const k_lds = k_base + ((t + 1) & 1) * kStageBytes;
-      if constexpr (CHECK) {
+  // Q^T as MFMA B operand: lane L holds query q0+L%32, features 8*(L/32)..+7
+  // of each 16-feature step.  Loaded once per query tile.
+  bf16x8 qf[kSteps];
+  // Start of a query tile: its first K, V and second K tiles go to LDS and
+  // its Q to registers.
+  auto begin_tile = [&](int lid_t) __attribute__((always_inline)) {
+    const int head_t = lid_t / n_qt;
+    const int qt_t = CAUSAL ? n_qt - 1 - lid_t % n_qt : lid_t % n_qt;
+    const size_t kv_off_t = ((size_t)head_t * Nk_all + kv_begin) * D;
+    const int nt = tiles_of(qt_t);
+    if (GENERAL && nt <= 0) return;
+    load_tile(k + kv_off_t, k_ld_off, kRegionK{}, 0, 0);
+    load_tile(v + kv_off_t, v_ld_off, kRegionV{}, 0, 0);
+    if (nt > 1) load_tile(k + kv_off_t, k_ld_off, kRegionK{}, 1, 1);
+    const int row = min(qt_t * kBlockM + wave * kQueriesPerWave + l32, N - 1);  // rows past N: any valid row
+    const __bf16* qrow = q + (size_t)head_t * N * D + (size_t)row * D + 8 * half;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          if (live(t + 1, sb)) {
-            scores_block<D>(k_lds, sb, k_off, qf, s_next[sb]);
+    for (int st = 0; st < kSteps; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st);
+  };
+  begin_tile(lid);
+
+  for (;;) {
+    const int head = lid / n_qt;
+    const int qt = CAUSAL ? n_qt - 1 - lid % n_qt : lid % n_qt;
+
+    const size_t head_off = (size_t)head * N * D;
+    const size_t kv_head_off = ((size_t)head * Nk_all + kv_begin) * D;
+    // SPLIT: this row's slot in the partial results.
+    const size_t part_row0 = SPLIT ? ((size_t)blockIdx.y * (grid / n_qt) + head) * N : 0;
+    const __bf16* const kh = k + kv_head_off;
+    const __bf16* const vh = v + kv_head_off;
+    const int q0 = qt * kBlockM + wave * kQueriesPerWave;  // this wave's first query
+
+    // Tiles this workgroup visits; tiles from first_mask on are masked:
+    // causal, the tiles on the diagonal of at least one of its waves; else
+    // only a last tile that runs past N.
+    const int n_tiles = tiles_of(qt);
+    int first_mask;
+    if constexpr (!GENERAL) {
+      first_mask = CAUSAL ? qt * (kBlockM / kBlockN) : (N % kBlockN ? n_tiles - 1 : n_tiles);
+    } else if constexpr (CAUSAL) {
+      // Tiles wholly at or below the workgroup's first query (+ off) need no mask.
+      const int first_last_key = qt * kBlockM + off;  // last key its first query sees
+      first_mask = first_last_key < 0 ? 0 : min((first_last_key + 1) / kBlockN, n_tiles);
+      const int kv_end = min((qt + 1) * kBlockM + off, Nk);
+      if (kv_end == Nk && Nk % kBlockN) first_mask = min(first_mask, n_tiles - 1);
+    } else {
+      first_mask = Nk % kBlockN ? n_tiles - 1 : n_tiles;
+    }
+    if constexpr (GENERAL) {
+      if (n_tiles <= 0) {  // no query of the workgroup sees a key
+        const int qrow = q0 + l32;
+        if (qrow < N) {
+          if constexpr (SPLIT) {
+            float* const prow = o_part + (part_row0 + qrow) * D;
+#pragma unroll
+            for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<f32x4*>(prow + 32 * b + 8 * j + 4 * half) = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (half == 0) lse_part[part_row0 + qrow] = -INFINITY;
           } else {
+            __bf16* const orow = o + head_off + (size_t)qrow * D;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s_next[sb][r] = -INFINITY;
+            for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * j + 4 * half) = bf16x4{0, 0, 0, 0};
+            if (half == 0) lse[(size_t)head * N + qrow] = -INFINITY;
           }
         }
-      } else {
-        scores<D>(k_lds, k_off, qf, s_next);
+        return;
       }
     }
-    // A row that has seen no key yet has m_ref = -inf and only -inf scores.
-    float mc = (GENERAL && m_ref == -INFINITY) ? 0.f : m_ref * c;
-    bf16x8 pb[2][2];
-    float l_tile = 0.f;
-    auto probs = [&]() __attribute__((always_inline)) {
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        if (CHECK && !live(t, sb)) continue;  // its probabilities are all 0
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          float p[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            p[j] = __builtin_amdgcn_exp2f(fmaf(s_cur[sb][8 * cc + j], c, -mc));
-            pb[sb][cc][j] = (__bf16)p[j];
-          }
-          l_tile += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        }
-      }
+
+    auto load_k = [&](int tile, int stage) __attribute__((always_inline)) {
+      load_tile(kh, k_ld_off, kRegionK{}, tile, stage);
     };
-    probs();
-    // Lazy rescale, checked on the probabilities themselves (the lane's tile
-    // sum; NaN and inf fail the test too).  Rare: the tile's exact maximum
-    // becomes the reference (lanes L and L^32 agree on it), O and l are
-    // rescaled and the probabilities formed again.  A row that has seen no
-    // key until now (m = -inf, general shapes) takes its first finite m here.
-    bool redo = !(l_tile <= kProbSumCap);
-    if constexpr (GENERAL) redo = redo || (m_ref == -INFINITY && l_tile > 0.f);
-    if (__builtin_amdgcn_ballot_w64(redo)) {
-      const float m_new = fmaxf(m_ref, tile_max(s_cur));
-      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c);
-      l_run *= alpha;
-#pragma unroll
-      for (int b = 0; b < kDBlocks; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
-      m_ref = m_new;
-      mc = (GENERAL && m_ref == -INFINITY) ? 0.f : m_ref * c;
-      l_tile = 0.f;
-      probs();
-    }
-    l_run += l_tile;
+    auto load_v = [&](int tile, int stage) __attribute__((always_inline)) {
+      load_tile(vh, v_ld_off, kRegionV{}, tile, stage);
+    };
 
-    __builtin_amdgcn_s_setprio(0);
-
-    // Phase B: O^T += V_t^T P_t^T on MFMA (and the mask of tile t+1 when it needs one).
-    const unsigned char* const v_lds = v_base + (t & 1) * kStageBytes;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      if (CHECK && !live(t, sb)) continue;
-#pragma unroll
-      for (int b = 0; b < kDBlocks; ++b)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const unsigned char* a = v_lds + (sb * 32 + cc * 16) * kRowBytes;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + v_block<D>(v_off[0], b)));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + v_block<D>(v_off[1], b)));
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[sb][cc], acc[b], 0, 0, 0);
-        }
-    }
-    if constexpr (HAS_NEXT) {
-      if constexpr (MASK_NEXT) mask_tile<CAUSAL>(s_next, (t + 1) * kBlockN, q0 + off, Nk, l32, half);
-    }
-  };
-  using yes = std::true_type;
-  using no = std::false_type;
-  auto copy_scores = [](f32x16(&dst)[2], const f32x16(&src)[2]) __attribute__((always_inline)) {
-    dst[0] = src[0];
-    dst[1] = src[1];
-  };
-
-  // Steps whose successor tile needs no mask run in pairs, so the two score
-  // buffers alternate without copies; the steps from first_mask-1 on mask
-  // their successor.
-  const int n_plain = first_mask - 1 > 0 ? first_mask - 1 : 0;
-  int t = 0;
-  for (; t + 1 < n_plain; t += 2) {
-    step(yes{}, no{}, t, s_a, s_b);
-    step(yes{}, no{}, t + 1, s_b, s_a);
-  }
-  if (t < n_plain) {
-    step(yes{}, no{}, t, s_a, s_b);
-    copy_scores(s_a, s_b);
-    ++t;
-  }
-  for (; t + 1 < n_tiles; ++t) {
-    step(yes{}, yes{}, t, s_a, s_b);
-    copy_scores(s_a, s_b);
-  }
-  step(no{}, no{}, t, s_a, s_b);  // the last tile has no successor
-
-  // Epilogue: O = acc / l, rounded to bf16; lse = (m*c + log2 l) * ln 2.
-  if (q0 + l32 >= N) return;  // a partial last query tile stores only rows < N
-  const float l_tot = pair_sum(l_run);
-  const float inv = (GENERAL && l_tot == 0.f) ? 0.f : 1.0f / l_tot;
-  const float row_lse = (GENERAL && l_tot == 0.f) ? -INFINITY : (m_ref * c + log2f(l_tot)) * kLn2;
-  if constexpr (SPLIT) {
-    float* const prow = o_part + (part_row0 + q0 + l32) * D;
+    f32x16 acc[kDBlocks];
 #pragma unroll
     for (int b = 0; b < kDBlocks; ++b)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4*>(prow + 32 * b + 8 * j + 4 * half) =
-            f32x4{acc[b][4 * j] * inv, acc[b][4 * j + 1] * inv, acc[b][4 * j + 2] * inv,
-                  acc[b][4 * j + 3] * inv};
-    if (half == 0) lse_part[part_row0 + q0 + l32] = row_lse;
-    return;
-  }
-  __bf16* const orow = o + head_off + (size_t)(q0 + l32) * D;
-#pragma unroll
-  for (int b = 0; b < kDBlocks; ++b) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x4 ov;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ov[r] = (__bf16)(acc[b][4 * j + r] * inv);
-      *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * j + 4 * half) = ov;
+      for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+
+    wait_lds_dma<0>();
+    __syncthreads();  // K0, V0, K1 have landed
+
+    if constexpr (GENERAL) {
+      // A wave whose 32 queries all lie past the last query (a short query
+      // block, e.g. decoding) computes nothing; it still issues its share of
+      // the copies and meets every barrier the tile loop below does.
+      if (q0 >= N) {
+        for (int t = 0; t < n_tiles; ++t) {
+          wait_lds_dma<0>();
+          __syncthreads();
+          if (t + 2 < n_tiles) load_k(t + 2, t & 1);
+          if (t + 1 < n_tiles) load_v(t + 1, (t + 1) & 1);
+        }
+        return;
+      }
     }
+
+    // Prologue: scores of tile 0 and the reference maximum, tile 0's (finite
+    // for every query in the square case, where tile 0 holds key 0).
+    f32x16 s_a[2], s_b[2];
+    scores<D>(k_base, k_off, qf, s_a);
+    if (first_mask == 0) mask_tile<CAUSAL>(s_a, 0, q0 + off, Nk, l32, half);
+    float m_ref = tile_max(s_a);  // reference maximum (raw score units), query q0+L%32
+    float l_run = 0.f;            // this lane's half of the normaliser
+
+    // One tile: s_cur holds tile t's (masked) scores, s_next receives tile
+    // t+1's.  HAS_NEXT and MASK_NEXT are compile-time so the body is straight
+    // line code the scheduler can interleave (MFMA of one phase against VALU).
+    // A 32-key block is live for this wave iff its first key is visible to at
+    // least one of the wave's queries; dead blocks (above the diagonal, or past
+    // N) skip their MFMAs and exponentials.  Only the steps that can meet one
+    // (masked successor, or the last tile) test this.
+    const int wave_last_key = CAUSAL ? min(q0 + kQueriesPerWave - 1 + off, Nk - 1) : Nk - 1;
+    auto live = [&](int tile, int sb) __attribute__((always_inline)) {
+      return tile * kBlockN + sb * 32 <= wave_last_key;
+    };
+    auto step = [&](auto has_next_tag, auto mask_next_tag, int t, f32x16(&s_cur)[2],
+                    f32x16(&s_next)[2]) __attribute__((always_inline)) {
+      constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
+      constexpr bool MASK_NEXT = decltype(mask_next_tag)::value;
+      constexpr bool CHECK = MASK_NEXT || !HAS_NEXT;  // may meet dead blocks
+      wait_lds_dma<0>();
+      __syncthreads();  // K_{t+1} and V_t have landed; K_t and V_{t-1} are free
+      if (t + 2 < n_tiles) load_k(t + 2, t & 1);
+      if (HAS_NEXT) load_v(t + 1, (t + 1) & 1);
+
+      // Phase A: probabilities of tile t (VALU) while S_{t+1} runs on MFMA.
+      // The wave runs this phase at raised issue priority: where the two waves
+      // of a SIMD contend, the one interleaving score MFMAs with the softmax
+      // goes first (measured 2-3 % faster than equal priorities).
+      __builtin_amdgcn_s_setprio(1);
+      if constexpr (HAS_NEXT) {
+        const unsigned char* const k_lds = k_base + ((t + 1) & 1) * kStageBytes;
+        if constexpr (CHECK) {
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) {
+            if (live(t + 1, sb)) {
+              scores_block<D>(k_lds, sb, k_off, qf, s_next[sb]);
+            } else {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) s_next[sb][r] = -INFINITY;
+            }
+          }
+        } else {
+          scores<D>(k_lds, k_off, qf, s_next);
+        }
+      }
+      // A row that has seen no key yet has m_ref = -inf and only -inf scores.
+      float mc = (GENERAL && m_ref == -INFINITY) ? 0.f : m_ref * c;
+      bf16x8 pb[2][2];
+      float l_tile = 0.f;
+      auto probs = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          if (CHECK && !live(t, sb)) continue;  // its probabilities are all 0
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            float p[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              p[j] = __builtin_amdgcn_exp2f(fmaf(s_cur[sb][8 * cc + j], c, -mc));
+              pb[sb][cc][j] = (__bf16)p[j];
+            }
+            l_tile += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+          }
+        }
+      };
+      probs();
+      // Lazy rescale, checked on the probabilities themselves (the lane's tile
+      // sum; NaN and inf fail the test too).  Rare: the tile's exact maximum
+      // becomes the reference (lanes L and L^32 agree on it), O and l are
+      // rescaled and the probabilities formed again.  A row that has seen no
+      // key until now (m = -inf, general shapes) takes its first finite m here.
+      bool redo = !(l_tile <= kProbSumCap);
+      if constexpr (GENERAL) redo = redo || (m_ref == -INFINITY && l_tile > 0.f);
+      if (__builtin_amdgcn_ballot_w64(redo)) {
+        const float m_new = fmaxf(m_ref, tile_max(s_cur));
+        const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+        l_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < kDBlocks; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
+        m_ref = m_new;
+        mc = (GENERAL && m_ref == -INFINITY) ? 0.f : m_ref * c;
+        l_tile = 0.f;
+        probs();
+      }
+      l_run += l_tile;
+
+      __builtin_amdgcn_s_setprio(0);
+
+      // Phase B: O^T += V_t^T P_t^T on MFMA (and the mask of tile t+1 when it needs one).
+      const unsigned char* const v_lds = v_base + (t & 1) * kStageBytes;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        if (CHECK && !live(t, sb)) continue;
+#pragma unroll
+        for (int b = 0; b < kDBlocks; ++b)
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const unsigned char* a = v_lds + (sb * 32 + cc * 16) * kRowBytes;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + v_block<D>(v_off[0], b)));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + v_block<D>(v_off[1], b)));
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[sb][cc], acc[b], 0, 0, 0);
+          }
+      }
+      if constexpr (HAS_NEXT) {
+        if constexpr (MASK_NEXT) mask_tile<CAUSAL>(s_next, (t + 1) * kBlockN, q0 + off, Nk, l32, half);
+      }
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    auto copy_scores = [](f32x16(&dst)[2], const f32x16(&src)[2]) __attribute__((always_inline)) {
+      dst[0] = src[0];
+      dst[1] = src[1];
+    };
+
+    // Steps whose successor tile needs no mask run in pairs, so the two score
+    // buffers alternate without copies; the steps from first_mask-1 on mask
+    // their successor.
+    const int n_plain = first_mask - 1 > 0 ? first_mask - 1 : 0;
+    int t = 0;
+    for (; t + 1 < n_plain; t += 2) {
+      step(yes{}, no{}, t, s_a, s_b);
+      step(yes{}, no{}, t + 1, s_b, s_a);
+    }
+    if (t < n_plain) {
+      step(yes{}, no{}, t, s_a, s_b);
+      copy_scores(s_a, s_b);
+      ++t;
+    }
+    for (; t + 1 < n_tiles; ++t) {
+      step(yes{}, yes{}, t, s_a, s_b);
+      copy_scores(s_a, s_b);
+    }
+    step(no{}, no{}, t, s_a, s_b);  // the last tile has no successor
+
+    // Epilogue: O = acc / l, rounded to bf16; lse = (m*c + log2 l) * ln 2.
+    const float l_tot = pair_sum(l_run);
+    const float inv = (GENERAL && l_tot == 0.f) ? 0.f : 1.0f / l_tot;
+    const float row_lse = (GENERAL && l_tot == 0.f) ? -INFINITY : (m_ref * c + log2f(l_tot)) * kLn2;
+    const int next = PERSIST ? lid_at(round + 1) : lid_end;  // ids only grow with the round
+    if constexpr (PERSIST) {
+      if (next < lid_end) {
+        __syncthreads();  // every wave is done reading this tile's LDS stages
+        begin_tile(next);
+      }
+    }
+    if (q0 + l32 < N) {  // a partial last query tile stores only rows < N
+      if constexpr (SPLIT) {
+        float* const prow = o_part + (part_row0 + q0 + l32) * D;
+#pragma unroll
+        for (int b = 0; b < kDBlocks; ++b)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<f32x4*>(prow + 32 * b + 8 * j + 4 * half) =
+                f32x4{acc[b][4 * j] * inv, acc[b][4 * j + 1] * inv, acc[b][4 * j + 2] * inv,
+                      acc[b][4 * j + 3] * inv};
+        if (half == 0) lse_part[part_row0 + q0 + l32] = row_lse;
+      } else {
+        __bf16* const orow = o + head_off + (size_t)(q0 + l32) * D;
+#pragma unroll
+        for (int b = 0; b < kDBlocks; ++b) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bf16x4 ov;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ov[r] = (__bf16)(acc[b][4 * j + r] * inv);
+            *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * j + 4 * half) = ov;
+          }
+        }
+        if (half == 0) lse[(size_t)head * N + q0 + l32] = row_lse;
+      }
+    }
+    if (!PERSIST || next >= lid_end) return;
+    lid = next;
+    ++round;
   }
-  if (half == 0) lse[(size_t)head * N + q0 + l32] = row_lse;
 }
 
 // Merge of the splits of one row: lse = ln sum_s exp(lse_s) and
@@ -664,6 +736,7 @@ constexpr int kMaxDevices = 64;
 
 struct DeviceInfo {
   bool gfx950 = false;
+  int n_cu = 0;  // compute units
 };
 
 std::once_flag g_once[kMaxDevices];
@@ -673,8 +746,10 @@ const DeviceInfo* device_info(int dev) {
   if (dev < 0 || dev >= kMaxDevices) return nullptr;
   std::call_once(g_once[dev], [dev] {
     hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) == hipSuccess)
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess) {
       g_info[dev].gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+      g_info[dev].n_cu = prop.multiProcessorCount;
+    }
   });
   return &g_info[dev];
 }
@@ -683,13 +758,24 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 template <int D, bool CAUSAL, bool GENERAL>
 int launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Nq, int Nk,
-           int off, float c, hipStream_t stream) {
+           int off, float c, int n_cu, hipStream_t stream) {
   const int n_qt = (Nq + Launch<D>::kBlockM - 1) / Launch<D>::kBlockM;
-  const int grid = n_qt * BH;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, GENERAL>), dim3(grid), dim3(Launch<D>::kThreads), 0,
+  const int n_work = n_qt * BH;
+  // Square problems at d=128 with more query tiles than CUs: one persistent
+  // workgroup per CU (the occupancy this head dim runs at).
+  if constexpr (D == 128 && !GENERAL) {
+    if (n_cu > 0 && n_work > n_cu) {
+      hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, false, true>), dim3(n_cu),
+                         dim3(Launch<D>::kThreads), 0, stream, static_cast<const __bf16*>(q),
+                         static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+                         static_cast<__bf16*>(o), lse, Nq, c, Nk, off, 0, nullptr, nullptr, n_work);
+      return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    }
+  }
+  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, GENERAL>), dim3(n_work), dim3(Launch<D>::kThreads), 0,
                      stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, Nq, c, Nk, off, 0,
-                     nullptr, nullptr);
+                     nullptr, nullptr, n_work);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -701,7 +787,7 @@ int launch_split(const void* q, const void* k, const void* v, void* o, float* ls
   hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, true, true>), dim3(n_qt * BH, n_splits),
                      dim3(Launch<D>::kThreads), 0, stream, static_cast<const __bf16*>(q),
                      static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
-                     static_cast<__bf16*>(o), lse, Nq, c, Nk, off, chunk, o_part, lse_part);
+                     static_cast<__bf16*>(o), lse, Nq, c, Nk, off, chunk, o_part, lse_part, n_qt * BH);
   const long long rows = (long long)BH * Nq;
   constexpr int kRowsPerBlock = 256 / (D / 4);
   hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
@@ -715,10 +801,13 @@ int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, i
              int Nk, int d, int causal, float scale, hipStream_t s) {
   const float c = scale * kLog2e;
   const int off = causal ? Nk - Nq : 0;
+  int dev = 0;
+  const DeviceInfo* info = hipGetDevice(&dev) == hipSuccess ? device_info(dev) : nullptr;
+  const int n_cu = info ? info->n_cu : 0;
   auto go = [&](auto d_tag) {
     constexpr int D = decltype(d_tag)::value;
-    return causal ? launch<D, true, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, s)
-                  : launch<D, false, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, s);
+    return causal ? launch<D, true, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, n_cu, s)
+                  : launch<D, false, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, n_cu, s);
   };
   switch (d) {
     case 32: return go(std::integral_constant<int, 32>{});
