@@ -756,16 +756,38 @@ const DeviceInfo* device_info(int dev) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Workgroups of the persistent square-shape kernel that fit on the GPU at
+// once (resident per CU, from the occupancy query, times the CU count);
+// cached per device.  0 if unknown.
+template <int D, bool CAUSAL>
+int persistent_grid(int dev, int n_cu) {
+  static std::once_flag once[kMaxDevices];
+  static int per_cu[kMaxDevices];
+  if (dev < 0 || dev >= kMaxDevices || n_cu <= 0) return 0;
+  std::call_once(once[dev], [dev] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &b, attn_fwd_kernel<D, CAUSAL, false, false, true>, Launch<D>::kThreads, 0) != hipSuccess)
+      b = 0;
+    per_cu[dev] = b;
+  });
+  return per_cu[dev] * n_cu;
+}
+
 template <int D, bool CAUSAL, bool GENERAL>
 int launch(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int Nq, int Nk,
-           int off, float c, int n_cu, hipStream_t stream) {
+           int off, float c, int dev, int n_cu, hipStream_t stream) {
   const int n_qt = (Nq + Launch<D>::kBlockM - 1) / Launch<D>::kBlockM;
   const int n_work = n_qt * BH;
-  // Square problems at d=128 with more query tiles than CUs: one persistent
-  // workgroup per CU (the occupancy this head dim runs at).
-  if constexpr (D == 128 && !GENERAL) {
-    if (n_cu > 0 && n_work > n_cu) {
-      hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, false, true>), dim3(n_cu),
+  // Square problems with more query tiles than fit on the GPU at once, at the
+  // head dims that run one workgroup per CU: one persistent workgroup per CU,
+  // so a CU is not idle while one workgroup drains and the next starts.
+  // Where several workgroups share a CU (d = 32, 64, 96) they already cover
+  // each other's start-up, and the persistent form measured slower.
+  if constexpr (!GENERAL && (D == 128 || D == 256)) {
+    const int grid = persistent_grid<D, CAUSAL>(dev, n_cu);
+    if (grid > 0 && n_work > grid) {
+      hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, false, true>), dim3(grid),
                          dim3(Launch<D>::kThreads), 0, stream, static_cast<const __bf16*>(q),
                          static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
                          static_cast<__bf16*>(o), lse, Nq, c, Nk, off, 0, nullptr, nullptr, n_work);
@@ -806,8 +828,8 @@ int dispatch(const void* q, const void* k, const void* v, void* o, float* lse, i
   const int n_cu = info ? info->n_cu : 0;
   auto go = [&](auto d_tag) {
     constexpr int D = decltype(d_tag)::value;
-    return causal ? launch<D, true, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, n_cu, s)
-                  : launch<D, false, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, n_cu, s);
+    return causal ? launch<D, true, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, dev, n_cu, s)
+                  : launch<D, false, GENERAL>(q, k, v, o, lse, BH, Nq, Nk, off, c, dev, n_cu, s);
   };
   switch (d) {
     case 32: return go(std::integral_constant<int, 32>{});

@@ -90,25 +90,27 @@ def test_workload_sampled(name):
     assert_parity(o_g, l_g, o_ref, lse_ref, f"{name} ({rows.size} rows)")
 
 
-# d=128 square problems with more 256-query tiles than the GPU has compute
-# units run one persistent workgroup per CU, each walking several query tiles
-# (the schedule's slots per XCD do not divide these tile counts, and the last
-# query tile of every head is partial).
+# Square problems at d=128 (256-query tiles) and d=256 (128-query tiles) with
+# more query tiles than the GPU has compute units run one persistent
+# workgroup per CU, each walking several query tiles (the schedule's slots per
+# XCD do not divide these tile counts, and the last query tile of every head
+# is partial).
 PERSISTENT = [
-    # B, H, N, causal
-    (1, 40, 1800, False),
-    (1, 40, 1800, True),
-    (3, 37, 777, True),
-    (2, 130, 300, False),
-    (1, 300, 256, True),
+    # B, H, N, d, causal
+    (1, 40, 1800, 128, False),
+    (1, 40, 1800, 128, True),
+    (3, 37, 777, 128, True),
+    (2, 130, 300, 128, False),
+    (1, 300, 256, 128, True),
+    (1, 20, 1700, 256, False),
+    (1, 20, 1700, 256, True),
 ]
 
 
-@pytest.mark.parametrize("B,H,N,causal", PERSISTENT)
-def test_persistent_sampled(B, H, N, causal):
+@pytest.mark.parametrize("B,H,N,d,causal", PERSISTENT)
+def test_persistent_sampled(B, H, N, d, causal):
     import torch
     import attention_attn_fwd_08_amd as af
-    d = 128
     log(f"[persistent] B={B} H={H} N={N} d={d} causal={causal}")
     q, k, v = make_qkv(B, H, N, d, seed=300 + H + N)
     scale = 1.0 / math.sqrt(d)
@@ -122,7 +124,7 @@ def test_persistent_sampled(B, H, N, causal):
     torch.cuda.synchronize()
     assert torch.equal(o2, o) and torch.equal(lse2, lse), "rows unwritten or results not repeatable"
     w = Workload("persistent", B, H, N, d, causal, seed=0)
-    rows = sample_rows(w, per_head=12, block=256)
+    rows = sample_rows(w, per_head=12, block=256 if d == 128 else 128)
     o_ref, lse_ref = oracle.attention_rows(q, k, v, causal, scale, rows, threads=ORACLE_THREADS)
     o_g = to_host_f64(o.reshape(-1, d)[rows])
     l_g = to_host_f64(lse.reshape(-1)[rows])
