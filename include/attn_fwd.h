@@ -68,8 +68,10 @@ enum attn_fwd_status {
  *
  * Ownership: the caller owns every buffer; the library allocates no device
  * memory and keeps no per-call state.  The only global state is a per-device
- * cache of the device's properties, filled once.  Calls are re-entrant and
- * may run concurrently on different streams.
+ * cache of the device's properties and of the kernels' resident workgroups
+ * per CU, each filled once (thread-safely) on the first call that needs it.
+ * Calls are re-entrant, may run concurrently on different streams, and may
+ * be captured in a HIP graph.
  *
  * Semantics: asynchronous.  ATTN_OK means the kernel was enqueued; results
  * are visible after the stream (or an event on it) is synchronised, and a
