@@ -8,7 +8,8 @@
 //   1. delta_i = rowsum(dO_i * O_i)                     (memory bound)
 //   2. per 128-key block: dV^T += dO^T P and dK^T += Q^T dS while Q and dO
 //      stream through LDS (S = Q K^T, dP = dO V^T, dS = P o (dP - delta));
-//      at d=128 dV and dK are computed by two workgroups per key block
+//      at d=128 and d=256 dV and dK are computed by two workgroups per key
+//      block (d=256: one workgroup per CU, one wave per SIMD)
 //   3. per 128-query block: dQ^T += K^T dS^T while K and V stream through
 //      LDS (S^T = K Q^T, dP^T = V dO^T)
 // Mapping to CDNA4, as in the forward kernel: v_mfma_f32_32x32x16_bf16 with
@@ -46,12 +47,17 @@ constexpr int kRows = 32;    // keys (kernel 2) or queries (kernel 3) per wave
 constexpr int kWaves = 4;    // waves per workgroup, one per SIMD
 constexpr int kBlock = kWaves * kRows;  // keys or queries per workgroup
 constexpr int kTile = 64;    // rows of a streamed LDS tile
+// Workgroups per CU the kernels are compiled for: two (two waves per SIMD,
+// 256 registers each) up to d=128; one at d=256, where a wave's operands and
+// accumulators need the SIMD's whole register file (512 per lane).
+template <int D>
+constexpr int kMinBlocks = D == 256 ? 1 : 2;
 constexpr int kXcds = 8;
 constexpr float kLog2e = 1.44269504088896340736f;
 
 template <int D>
 struct Geo {
-  static_assert(D == 32 || D == 64 || D == 96 || D == 128, "unsupported head dim");
+  static_assert(D == 32 || D == 64 || D == 96 || D == 128 || D == 256, "unsupported head dim");
   static constexpr int kRowBytes = D * 2;
   static constexpr int kSteps = D / 16;    // MFMA k-steps over the head dimension
   static constexpr int kDBlocks = D / 32;  // 32-row blocks of a transposed accumulator
@@ -62,14 +68,16 @@ struct Geo {
 // 16-byte chunk of 16 consecutive rows) needs the 16 rows in 16 distinct
 // bank groups; a transposed read (32 lanes read 4 rows x 4 adjacent chunks)
 // needs those 16 (row, chunk) pairs distinct.  d=128 (256-byte rows):
-// 4*(row%4) + 2*(row/4 %2) + (row/8 %2).  d=64 (128-byte rows, two per bank
+// 4*(row%4) + 2*(row/4 %2) + (row/8 %2); d=256 (512-byte rows, so chunks c
+// and c+16 of a row share a bank group) uses the same XOR on the low four
+// chunk bits.  d=64 (128-byte rows, two per bank
 // sweep): 4*(row/2 %2) + (row/4 %4).  d=32 and d=96 (rows of 4 and 12
 // chunks: rows r, r+4, r+8, r+12 share a bank group, the residues of r mod 4
 // use disjoint ones, and the 4 rows of a transposed read already fall in 4
 // distinct bank quarters): (row/4 %4), which keeps a chunk in its group of 4.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128) return 4 * (row & 3) + 2 * ((row >> 2) & 1) + ((row >> 3) & 1);
+  if constexpr (D == 128 || D == 256) return 4 * (row & 3) + 2 * ((row >> 2) & 1) + ((row >> 3) & 1);
   else if constexpr (D == 64) return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
   else return (row >> 2) & 3;
 }
@@ -151,6 +159,20 @@ __device__ __forceinline__ int tr_off(int lane, int h, int b, int cc) {
   const int col = 32 * b + 16 * (g16 & 1) + 4 * (s16 & 3);
   return r * Geo<D>::kRowBytes + (((col >> 3) ^ swz<D>(r)) << 4) + (col & 7) * 2;
 }
+// Transposed-read offsets are held per workgroup as tro[cc][b][h] =
+// tr_off(lane, h, b, cc).  At d=256 only block 0's are filled and read
+// (kTroBlocks): with 512-byte rows the row, the 16-byte chunk and the place in
+// the chunk occupy disjoint bits of an offset, and block b's chunk is block
+// 0's XOR 4b (the swizzle changes the low four chunk bits only), so block b's
+// offset is block 0's XOR (b << 6) (tro_xor).  That keeps 28 registers free
+// in kernels that hold the whole register file.
+template <int D>
+constexpr int kTroBlocks = D == 256 ? 1 : Geo<D>::kDBlocks;
+template <int D>
+constexpr int tro_block(int b) { return D == 256 ? 0 : b; }
+template <int D>
+constexpr int tro_xor(int b) { return D == 256 ? b << 6 : 0; }
+
 __device__ __forceinline__ bf16x8 read_tr(const unsigned char* base, int off_lo, int off_hi) {
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off_lo));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off_hi));
@@ -224,7 +246,8 @@ constexpr int dkdv_smem_bytes() { return 2 * (2 * kQT * D * 2 + 2 * kQT * 4); } 
 // and the scores in the registers of two waves per SIMD, so the parts run as
 // separate workgroups: S is formed twice, but every workgroup runs at two
 // waves per SIMD (measured: about 18 % less time than one combined wave per
-// SIMD).
+// SIMD).  At d=256 the dK part alone (K, V, the dK accumulator and the
+// scores) needs ~350 registers, so the parts run at one wave per SIMD.
 //
 // GENERAL: Nq queries against Nk keys, causal mask offset by `off` (key j
 // visible to query i iff j <= i + off); otherwise Nk = Nq and off = 0.
@@ -289,7 +312,7 @@ __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-    for (int b = 0; b < kDBlocks; ++b)
+    for (int b = 0; b < kTroBlocks<D>; ++b)
 #pragma unroll
       for (int h = 0; h < 2; ++h) tro[cc][b][h] = tr_off<D>(lane, h, b, cc);
 
@@ -379,8 +402,8 @@ __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int b = 0; b < kDBlocks; ++b) {
-          if (kDoV) dvt[b] = mfma(read_tr(da, tro[cc][b][0], tro[cc][b][1]), pb[cc], dvt[b]);
-          if (kDoK) dkt[b] = mfma(read_tr(qa, tro[cc][b][0], tro[cc][b][1]), sb[cc], dkt[b]);
+          if (kDoV) dvt[b] = mfma(read_tr(da, tro[cc][tro_block<D>(b)][0] ^ tro_xor<D>(b), tro[cc][tro_block<D>(b)][1] ^ tro_xor<D>(b)), pb[cc], dvt[b]);
+          if (kDoK) dkt[b] = mfma(read_tr(qa, tro[cc][tro_block<D>(b)][0] ^ tro_xor<D>(b), tro[cc][tro_block<D>(b)][1] ^ tro_xor<D>(b)), sb[cc], dkt[b]);
         }
     };
 
@@ -442,11 +465,11 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                    logical_block());
 }
 
-// d=128: two workgroups per key block, one for dV and one for dK.  Logical
+// d=128 and d=256: two workgroups per key block, one for dV and one for dK.  Logical
 // ids 2b and 2b+1 are the two parts of key block b, so they run side by side
 // on one XCD and share the Q and dO tiles in its L2.
 template <int D, bool CAUSAL, bool GENERAL>
-__global__ __launch_bounds__(kWaves * kWave, 2)
+__global__ __launch_bounds__(kWaves * kWave, kMinBlocks<D>)
 void bwd_dkdv_split_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                            const __bf16* __restrict__ v, const float* __restrict__ lse,
                            const __bf16* __restrict__ dout, const float* __restrict__ delta,
@@ -466,7 +489,7 @@ void bwd_dkdv_split_kernel(const __bf16* __restrict__ q, const __bf16* __restric
 // Kernel 3: dQ for one 128-query block of one head (32 queries per wave).
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool GENERAL>
-__global__ __launch_bounds__(kWaves * kWave, 2)
+__global__ __launch_bounds__(kWaves * kWave, kMinBlocks<D>)
 void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                    const __bf16* __restrict__ v, const float* __restrict__ lse,
                    const __bf16* __restrict__ dout, const float* __restrict__ delta,
@@ -527,7 +550,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-    for (int b = 0; b < kDBlocks; ++b)
+    for (int b = 0; b < kTroBlocks<D>; ++b)
 #pragma unroll
       for (int h = 0; h < 2; ++h) tro[cc][b][h] = tr_off<D>(lane, h, b, cc);
 
@@ -584,7 +607,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int b = 0; b < kDBlocks; ++b)
-          dqt[b] = mfma(read_tr(ka, tro[cc][b][0], tro[cc][b][1]), sbf[cc], dqt[b]);
+          dqt[b] = mfma(read_tr(ka, tro[cc][tro_block<D>(b)][0] ^ tro_xor<D>(b), tro[cc][tro_block<D>(b)][1] ^ tro_xor<D>(b)), sbf[cc], dqt[b]);
     };
     const bool partial =
         kt * kTile + kTile - 1 > wave_last_key || (CAUSAL && kt * kTile + kTile - 1 > q0 + off);
@@ -649,7 +672,7 @@ int launch(const void* q, const void* k, const void* v, const void* o, const flo
   const int n_kblk = (Nk + kBlock - 1) / kBlock;
   const int n_qblk = (Nq + kBlock - 1) / kBlock;
   if (n_kblk > 0) {
-    if constexpr (D == 128)
+    if constexpr (D == 128 || D == 256)
       hipLaunchKernelGGL((bwd_dkdv_split_kernel<D, CAUSAL, GENERAL>), dim3(2 * n_kblk * BH),
                          dim3(kWaves * kWave), 0, stream, static_cast<const __bf16*>(q),
                          static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), lse,
@@ -679,7 +702,7 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
               int B, int H, int Nq, int Nk, int d, float scale, bool* nothing) {
   *nothing = false;
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0) return ATTN_ERR_SHAPE;
-  if (d != 32 && d != 64 && d != 96 && d != 128) return ATTN_ERR_HEAD_DIM;
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return ATTN_ERR_HEAD_DIM;
   if (!(scale > 0.0f) || !isfinite(scale)) return ATTN_ERR_SCALE;
   const int64_t bh = (int64_t)B * H;
   if (bh > INT32_MAX) return ATTN_ERR_SHAPE;
@@ -717,7 +740,8 @@ int dispatch(const void* q, const void* k, const void* v, const void* o, const f
     case 32: return go(std::integral_constant<int, 32>{});
     case 64: return go(std::integral_constant<int, 64>{});
     case 96: return go(std::integral_constant<int, 96>{});
-    default: return go(std::integral_constant<int, 128>{});
+    case 128: return go(std::integral_constant<int, 128>{});
+    default: return go(std::integral_constant<int, 256>{});
   }
 }
 

@@ -46,7 +46,12 @@
 //     kernel; waves whose queries all lie past Nq only copy and wait;
 //   * workgroup ids are remapped so that tiles of one head run on one XCD
 //     (workgroups are dispatched round-robin over the 8 XCDs), keeping that
-//     head's K/V in the XCD's L2; causal tiles of a head run longest first.
+//     head's K/V in the XCD's L2; causal tiles of a head run longest first;
+//   * at d=128 and d=256, where one workgroup fills a CU, square problems
+//     with more query tiles than CUs run one persistent workgroup per CU:
+//     it walks its XCD's tiles and issues the next tile's K/V/Q loads before
+//     storing the current tile's output, so the CU does not idle between
+//     tiles; causal rounds alternate long and short tiles per workgroup.
 
 #include <hip/hip_runtime.h>
 
@@ -938,7 +943,7 @@ extern "C" const char* attn_fwd_strerror(int status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "a required pointer is NULL";
     case ATTN_ERR_SHAPE: return "B, H or N is negative, or the problem size overflows";
-    case ATTN_ERR_HEAD_DIM: return "head dimension d must be 32, 64, 96, 128 or 256 (backward: 32, 64, 96 or 128)";
+    case ATTN_ERR_HEAD_DIM: return "head dimension d must be 32, 64, 96, 128 or 256";
     case ATTN_ERR_SEQ_MULTIPLE: return "reserved (any sequence length is accepted)";
     case ATTN_ERR_ALIGN: return "q, k, v, o and lse must be 16-byte aligned";
     case ATTN_ERR_SCALE: return "scale must be finite and greater than 0";

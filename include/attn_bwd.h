@@ -43,7 +43,7 @@ extern "C" {
  *            also the library's only intermediate (read back by the later
  *            kernels of the same call), so it must not alias any other
  *            argument.
- *   B, H, N, d, causal, scale: as for attn_fwd (d = 32, 64, 96 or 128, any N >= 0).
+ *   B, H, N, d, causal, scale: as for attn_fwd (d = 32, 64, 96, 128 or 256, any N >= 0).
  *   stream   a hipStream_t cast to void*; NULL means the default stream.
  *
  * All pointers are 16-byte aligned device pointers; outputs must not overlap

@@ -147,7 +147,7 @@ def call_bwd(B=2, H=3, N=256, d=128, causal=0, scale=0.088, **ptrs):
     (dict(B=-1), af.Status.ERR_SHAPE),
     (dict(N=-1), af.Status.ERR_SHAPE),
     (dict(d=48), af.Status.ERR_HEAD_DIM),
-    (dict(d=256), af.Status.ERR_HEAD_DIM),
+    (dict(d=512), af.Status.ERR_HEAD_DIM),
     (dict(scale=0.0), af.Status.ERR_SCALE),
     (dict(scale=float("nan")), af.Status.ERR_SCALE),
     (dict(B=1, H=1, N=1 << 24, d=128), af.Status.ERR_SHAPE),
@@ -292,7 +292,7 @@ def call_bwd_ex(B=2, H=3, Nq=100, Nk=300, d=128, causal=1, scale=0.088, **ptrs):
 @pytest.mark.parametrize("kw,status", [
     (dict(Nq=-1), af.Status.ERR_SHAPE),
     (dict(Nk=-1), af.Status.ERR_SHAPE),
-    (dict(d=256), af.Status.ERR_HEAD_DIM),
+    (dict(d=16), af.Status.ERR_HEAD_DIM),
     (dict(scale=0.0), af.Status.ERR_SCALE),
     (dict(Nk=1 << 24), af.Status.ERR_SHAPE),
     (dict(Nq=1 << 24), af.Status.ERR_SHAPE),

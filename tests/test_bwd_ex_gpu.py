@@ -24,7 +24,7 @@ SHAPES = [
     (2, 1, 64, 1000, 128, True), (1, 3, 1, 777, 128, False),
     (1, 1, 513, 257, 64, False), (1, 2, 200, 450, 64, True),
     (1, 1, 77, 33, 128, True), (1, 2, 100, 300, 32, True), (1, 2, 300, 130, 96, True),
-    (1, 1, 64, 500, 96, False),
+    (1, 1, 64, 500, 96, False), (1, 2, 100, 300, 256, True), (1, 1, 300, 130, 256, True),
 ]
 
 

@@ -64,6 +64,7 @@ SHAPES = [
     (1, 1, 31, 64, True), (1, 1, 33, 128, True),
     (2, 1, 200, 128, True), (1, 2, 333, 64, False), (1, 1, 1000, 128, True),
     (1, 2, 256, 32, False), (2, 1, 333, 32, True), (1, 2, 256, 96, True), (1, 1, 700, 96, False),
+    (1, 2, 256, 256, False), (1, 2, 256, 256, True), (2, 1, 333, 256, True), (1, 1, 700, 256, False),
 ]
 
 
