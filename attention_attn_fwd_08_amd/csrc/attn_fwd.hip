@@ -403,7 +403,7 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     v_off[h] = r * kRowBytes + (((col >> 3) ^ v_swz<D>(r)) << 4) + (col & 7) * 2;
   }
 
-  // Last key tile (exclusive) a query tile visits.
+  // Number of key tiles a query tile visits (causal: up to its last query).
   auto tiles_of = [&](int qt) __attribute__((always_inline)) {
     const int kv_end = CAUSAL ? min((qt + 1) * kBlockM + off, Nk) : Nk;
     return (kv_end + kBlockN - 1) / kBlockN;
