@@ -62,7 +62,8 @@ def test_random_forward(B, H, Nq, Nk, d, causal, seed):
     _check_fwd(o2, lse2, o_ref, lse_ref)
 
 
-@pytest.mark.parametrize("B,H,Nq,Nk,d,causal,seed", _cases(20, 72, [32, 64, 96, 128]))
+@pytest.mark.parametrize("B,H,Nq,Nk,d,causal,seed",
+                         _cases(20, 72, [32, 64, 96, 128]) + _cases(6, 73, [256]))
 def test_random_backward(B, H, Nq, Nk, d, causal, seed):
     import torch
     import attention_attn_fwd_08_amd as af
