@@ -11,6 +11,9 @@ SOURCE = os.path.join(PKG, "csrc", "attn_fwd.hip")
 SOURCES = (SOURCE, os.path.join(PKG, "csrc", "attn_bwd.hip"), os.path.join(PKG, "csrc", "gemm.hip"))
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libattn_fwd.so")
+# Debug build of the forward alone: LDS filled with NaN before any copy
+# lands (tests compare it bit for bit with the library).
+POISON_LIBRARY = os.path.join(PKG, "libattn_fwd_lds_poison.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 instructions are switched off for all device code.
@@ -22,10 +25,17 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Build libattn_fwd.so in the package directory; returns its path."""
+    """Build libattn_fwd.so (and the LDS-poison debug build of the forward)
+    in the package directory; returns the library's path."""
+    _compile(LIBRARY, list(SOURCES), [], verbose)
+    _compile(POISON_LIBRARY, [SOURCE], ["-DATTN_DEBUG_POISON_LDS"], verbose)
+    return LIBRARY
+
+
+def _compile(out: str, sources: list, extra: list, verbose: bool) -> None:
     fd, tmp = tempfile.mkstemp(suffix=".so.tmp", dir=PKG)
     os.close(fd)
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-o", tmp, *SOURCES]
+    cmd = [HIPCC, *FLAGS, *extra, "-I", INCLUDE, "-o", tmp, *sources]
     try:
         res = subprocess.run(cmd, capture_output=True, text=True)
         noise = "is not a recognized feature for this target"
@@ -34,11 +44,10 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
         if verbose and msgs:
             print("\n".join(msgs))
-        os.replace(tmp, LIBRARY)
+        os.replace(tmp, out)
     finally:
         if os.path.exists(tmp):
             os.unlink(tmp)
-    return LIBRARY
 
 
 if __name__ == "__main__":

@@ -427,6 +427,13 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st);
   };
+#ifdef ATTN_DEBUG_POISON_LDS
+  // Debug build: every LDS byte starts as a NaN pattern, so an operand read
+  // of a location no copy has written turns the output into NaN.
+  for (int i = tid; i < (int)(sizeof(smem) / 4); i += Launch<D>::kThreads)
+    reinterpret_cast<unsigned*>(smem)[i] = 0x7fc07fc0u;
+  __syncthreads();
+#endif
   begin_tile(lid);
 
   for (;;) {

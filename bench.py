@@ -55,6 +55,8 @@ from attention_attn_fwd_08_amd.inputs import (HEADLINE, WORKLOADS, Workload, mak
 PEAK_BF16_TFLOPS = 2516.6
 KERNEL_SOURCE = os.path.join(ROOT, "attention_attn_fwd_08_amd", "csrc", "attn_fwd.hip")
 GEMM_SOURCE = os.path.join(ROOT, "attention_attn_fwd_08_amd", "csrc", "gemm.hip")
+BWD_SOURCE = os.path.join(ROOT, "attention_attn_fwd_08_amd", "csrc", "attn_bwd.hip")
+GOLDEN_DIGESTS = os.path.join(ROOT, "tests", "golden", "inputs_sha256.json")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 O_MAX_TOL, O_MEAN_TOL, LSE_MAX_TOL = 2e-2, 2e-3, 1e-3
@@ -82,6 +84,22 @@ def measured_traffic(entry_name: str, source: str = KERNEL_SOURCE):
     if not entry or entry.get("source_sha256") != source_sha(source):
         return None
     return entry.get("hbm_bytes_per_launch")
+
+
+def inputs_provenance(name: str, bits: dict) -> dict:
+    """SHA-256 of each input buffer (bf16 bits), whether they equal the
+    committed digests of the workload (a guard against generator drift), and
+    the kernel sources' digests."""
+    import numpy as np
+    digests = {k: hashlib.sha256(memoryview(np.ascontiguousarray(b))).hexdigest() for k, b in bits.items()}
+    try:
+        with open(GOLDEN_DIGESTS) as f:
+            golden = json.load(f).get(name)
+    except (OSError, ValueError):
+        golden = None
+    match = None if golden is None else all(golden.get(k) == v for k, v in digests.items())
+    return {"inputs_sha256": digests, "inputs_match_committed_digests": match,
+            "kernel_sources_sha256": {os.path.basename(p): source_sha(p) for p in (KERNEL_SOURCE, BWD_SOURCE)}}
 
 
 def cpu_model() -> str:
@@ -437,6 +455,7 @@ def main() -> int:
     else:
         q_bits, k_bits, v_bits = workload_inputs(w)
     log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+    provenance = inputs_provenance(w.name, {"q": q_bits, "k": k_bits, "v": v_bits})
 
     def dev_tensor(bits):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -531,6 +550,7 @@ def main() -> int:
             "pass": args.which,
         },
         "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "provenance": provenance,
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),

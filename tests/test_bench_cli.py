@@ -54,3 +54,18 @@ def test_committed_traffic_entries_name_their_sources():
 
 def test_cpu_model_is_a_string():
     assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+
+
+def test_inputs_provenance_matches_committed_digests():
+    from attention_attn_fwd_08_amd.inputs import WORKLOADS, workload_inputs
+    w = WORKLOADS["B1-H1-N256-d64"]
+    q, k, v = workload_inputs(w)
+    rec = bench.inputs_provenance(w.name, {"q": q, "k": k, "v": v})
+    assert rec["inputs_match_committed_digests"] is True
+    assert rec["inputs_sha256"]["q"] == hashlib.sha256(q.tobytes()).hexdigest()
+    assert set(rec["kernel_sources_sha256"]) == {"attn_fwd.hip", "attn_bwd.hip"}
+    # A changed buffer (one bf16 value) no longer matches; an unknown workload has no digests.
+    q2 = q.copy()
+    q2.flat[7] ^= 1
+    assert bench.inputs_provenance(w.name, {"q": q2, "k": k, "v": v})["inputs_match_committed_digests"] is False
+    assert bench.inputs_provenance("no-such-workload", {"q": q})["inputs_match_committed_digests"] is None
