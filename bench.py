@@ -573,6 +573,7 @@ def main() -> int:
     elif not args.no_cpu_baseline and args.which == "bwd":
         log("backward oracle on one head ...")
         rec, ref = cpu_baseline_bwd(w, q_bits, k_bits, v_bits, g_bits, 1)
+        rec["gpu_over_cpu"] = round(value / rec["value"], 1) if rec["value"] > 0 else None
         result["cpu_baseline"] = rec
         result["roofline"]["unit_of_launch"] = "whole backward: delta, dK/dV and dQ kernels"
         parity = {"heads": 1}
@@ -590,6 +591,7 @@ def main() -> int:
         log(f"oracle sample on {threads} host threads ...")
         rec, rows, o_ref, lse_ref = cpu_baseline(w, q_bits, k_bits, v_bits, args.cpu_gflop,
                                                  threads)
+        rec["gpu_over_cpu"] = round(value / rec["value"], 1) if rec["value"] > 0 else None
         result["cpu_baseline"] = rec
         o_g = o.reshape(-1, w.d)[torch.from_numpy(rows).to(dev)].float().cpu().numpy()
         l_g = lse.reshape(-1)[torch.from_numpy(rows).to(dev)].cpu().numpy()
