@@ -47,8 +47,8 @@
 //   * workgroup ids are remapped so that tiles of one head run on one XCD
 //     (workgroups are dispatched round-robin over the 8 XCDs), keeping that
 //     head's K/V in the XCD's L2; causal tiles of a head run longest first;
-//   * at d=128 and d=256, where one workgroup fills a CU, square problems
-//     with more query tiles than CUs run one persistent workgroup per CU:
+//   * at d=128 and d=256, where one workgroup fills a CU, problems with
+//     more query tiles than CUs run one persistent workgroup per CU:
 //     it walks its XCD's tiles and issues the next tile's K/V/Q loads before
 //     storing the current tile's output, so the CU does not idle between
 //     tiles; causal rounds alternate long and short tiles per workgroup.
@@ -280,7 +280,7 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
 // blockIdx.y takes only keys [y*kv_chunk, (y+1)*kv_chunk) and writes its
 // normalised partial O (fp32) and partial lse to o_part / lse_part, laid out
 // [split, head, query, d] and [split, head, query]; a merge kernel combines
-// the splits.  PERSIST (square shapes only): the grid is one workgroup per
+// the splits.  PERSIST (not with SPLIT): the grid is one workgroup per
 // resident slot and each workgroup walks n_work query tiles' worth of
 // logical ids; the next tile's K/V/Q loads are issued before the current
 // tile's output is stored, so a tile's start-up overlaps the previous
@@ -293,7 +293,7 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      int kv_chunk, float* __restrict__ o_part, float* __restrict__ lse_part,
                      int n_work) {
   static_assert(!SPLIT || GENERAL, "a split is a general-shape problem");
-  static_assert(!PERSIST || !GENERAL, "the persistent walk is for square shapes");
+  static_assert(!PERSIST || !SPLIT, "split workgroups are not persistent");
   const int Nk_all = GENERAL ? nk_arg : N;
   const int kv_begin = SPLIT ? (int)blockIdx.y * kv_chunk : 0;  // first key of this split
   const int Nk = SPLIT ? min(kv_chunk, Nk_all - kv_begin) : Nk_all;
@@ -486,10 +486,12 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
             if (half == 0) lse[(size_t)head * N + qrow] = -INFINITY;
           }
         }
-        return;
+        if constexpr (PERSIST) goto next_tile;
+        else return;
       }
     }
 
+    {  // the tile's computation (persistent general-shape exits jump past it)
     auto load_k = [&](int tile, int stage) __attribute__((always_inline)) {
       load_tile(kh, k_ld_off, kRegionK{}, tile, stage);
     };
@@ -517,7 +519,8 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
           if (t + 2 < n_tiles) load_k(t + 2, t & 1);
           if (t + 1 < n_tiles) load_v(t + 1, (t + 1) & 1);
         }
-        return;
+        if constexpr (PERSIST) goto next_tile;
+        else return;
       }
     }
 
@@ -703,6 +706,20 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     if (!PERSIST || next >= lid_end) return;
     lid = next;
     ++round;
+    continue;
+    }
+  next_tile: __attribute__((unused));
+    // A persistent workgroup that computed nothing for this tile (general
+    // shapes: no query sees a key, or waves past the last query) goes on to
+    // the next tile with the same barrier as the others.
+    if constexpr (PERSIST) {
+      const int nxt = lid_at(round + 1);
+      if (nxt >= lid_end) return;
+      __syncthreads();  // every wave is done reading this tile's LDS stages
+      begin_tile(nxt);
+      lid = nxt;
+      ++round;
+    }
   }
 }
 
@@ -768,10 +785,10 @@ const DeviceInfo* device_info(int dev) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Workgroups of the persistent square-shape kernel that fit on the GPU at
+// Workgroups of the persistent kernel that fit on the GPU at
 // once (resident per CU, from the occupancy query, times the CU count);
 // cached per device.  0 if unknown.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool GENERAL>
 int persistent_grid(int dev, int n_cu) {
   static std::once_flag once[kMaxDevices];
   static int per_cu[kMaxDevices];
@@ -779,7 +796,7 @@ int persistent_grid(int dev, int n_cu) {
   std::call_once(once[dev], [dev] {
     int b = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &b, attn_fwd_kernel<D, CAUSAL, false, false, true>, Launch<D>::kThreads, 0) != hipSuccess)
+            &b, attn_fwd_kernel<D, CAUSAL, GENERAL, false, true>, Launch<D>::kThreads, 0) != hipSuccess)
       b = 0;
     per_cu[dev] = b;
   });
@@ -791,15 +808,15 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
            int off, float c, int dev, int n_cu, hipStream_t stream) {
   const int n_qt = (Nq + Launch<D>::kBlockM - 1) / Launch<D>::kBlockM;
   const int n_work = n_qt * BH;
-  // Square problems with more query tiles than fit on the GPU at once, at the
+  // Problems with more query tiles than fit on the GPU at once, at the
   // head dims that run one workgroup per CU: one persistent workgroup per CU,
   // so a CU is not idle while one workgroup drains and the next starts.
   // Where several workgroups share a CU (d = 32, 64, 96) they already cover
   // each other's start-up, and the persistent form measured slower.
-  if constexpr (!GENERAL && (D == 128 || D == 256)) {
-    const int grid = persistent_grid<D, CAUSAL>(dev, n_cu);
+  if constexpr (D == 128 || D == 256) {
+    const int grid = persistent_grid<D, CAUSAL, GENERAL>(dev, n_cu);
     if (grid > 0 && n_work > grid) {
-      hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, false, false, true>), dim3(grid),
+      hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, GENERAL, false, true>), dim3(grid),
                          dim3(Launch<D>::kThreads), 0, stream, static_cast<const __bf16*>(q),
                          static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
                          static_cast<__bf16*>(o), lse, Nq, c, Nk, off, 0, nullptr, nullptr, n_work);

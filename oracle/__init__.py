@@ -274,6 +274,19 @@ def attention_ex(q, k, v, causal: bool, scale: float, threads: int = 1,
     j <= i + Nk - Nq.  Rows that see no key give o = 0, lse = -inf.
     Returns ``o`` float64 [B,H,Nq,d] and ``lse`` float64 [B,H,Nq].
     """
+    B, H, Nq, d = np.shape(q)
+    o, lse = attention_ex_rows(q, k, v, causal, scale, np.arange(B * H * Nq, dtype=np.int64),
+                               threads=threads, lib=lib)
+    return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
+
+
+def attention_ex_rows(q, k, v, causal: bool, scale: float, rows, threads: int = 1,
+                      lib: ctypes.CDLL | None = None):
+    """:func:`attention_ex` for the listed query rows only.
+
+    ``rows`` holds flat row indices r = (b*H + h)*Nq + i.  Returns ``(o, lse)``
+    with ``o`` float64 [len(rows), d] and ``lse`` float64 [len(rows)].
+    """
     for name, a in (("q", q), ("k", k), ("v", v)):
         if not isinstance(a, np.ndarray) or a.dtype != np.uint16 or a.ndim != 4:
             raise TypeError(f"{name} must be a 4-D numpy uint16 array of bf16 bits")
@@ -282,8 +295,10 @@ def attention_ex(q, k, v, causal: bool, scale: float, threads: int = 1,
     if k.shape != v.shape or k.shape[:2] != (B, H) or k.shape[3] != d:
         raise ValueError("k and v must be [B, H, Nk, d] matching q's B, H and d")
     Nk = k.shape[2]
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+    if rows.size and (rows.min() < 0 or rows.max() >= B * H * Nq):
+        raise ValueError("row index out of range")
     lib = lib or load()
-    rows = np.arange(B * H * Nq, dtype=np.int64)
     o = np.zeros((rows.size, d)); lse = np.zeros(rows.size)
     threads = max(1, min(int(threads), rows.size or 1))
     bounds = np.linspace(0, rows.size, threads + 1).astype(np.int64)
@@ -305,7 +320,7 @@ def attention_ex(q, k, v, causal: bool, scale: float, threads: int = 1,
             statuses = list(pool.map(run, range(threads)))
     if any(s != 0 for s in statuses):
         raise RuntimeError(f"oracle failed with status {statuses}")
-    return o.reshape(B, H, Nq, d), lse.reshape(B, H, Nq)
+    return o, lse
 
 
 def attention_bwd_ex(q, k, v, dout, causal: bool, scale: float, threads: int = 1,

@@ -142,3 +142,19 @@ def test_ex_mutant_is_caught(name, tmp_path):
         except (AssertionError, RuntimeError, FloatingPointError, ValueError) as e:
             caught.append((pin.__name__, str(e)[:80]))
     assert caught, f"no pin detects the mutation '{name}'"
+
+
+@pytest.mark.parametrize("Nq,Nk,causal", [(37, 90, True), (90, 37, True), (50, 50, False)])
+def test_ex_rows_subset_equals_full(Nq, Nk, causal):
+    """Row selection only: the listed rows of the full general-shape result,
+    bit for bit, in the order listed (rows with no visible key included)."""
+    rng = np.random.default_rng(Nq * 7 + Nk)
+    mk = lambda n: f32_to_bf16_bits(rng.standard_normal((2, 3, n, 16)).astype(np.float32))  # noqa: E731
+    q, k, v = mk(Nq), mk(Nk), mk(Nk)
+    o, lse = oracle.attention_ex(q, k, v, causal, 0.25)
+    rows = rng.choice(2 * 3 * Nq, size=25, replace=False)
+    o_r, lse_r = oracle.attention_ex_rows(q, k, v, causal, 0.25, rows, threads=3)
+    assert np.array_equal(o_r, o.reshape(-1, 16)[rows])
+    assert np.array_equal(lse_r, lse.reshape(-1)[rows])
+    with pytest.raises(ValueError):
+        oracle.attention_ex_rows(q, k, v, causal, 0.25, [2 * 3 * Nq])
