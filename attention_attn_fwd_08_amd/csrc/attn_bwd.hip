@@ -103,6 +103,15 @@ __device__ __forceinline__ void load16_to_lds(i32x4 rsrc, int voff, unsigned lds
 }
 #pragma clang diagnostic pop
 __device__ __forceinline__ void wait_lds_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The same wait through the compiler builtin, which the compiler's own
+// wait-count bookkeeping sees (vmcnt 0; expcnt and lgkmcnt left at their
+// maxima, 7 and 15).  Issued once before a tile loop whose MFMAs read
+// registers loaded from global memory before it: without it the compiler
+// cannot tell inside the loop that those loads have landed, and counts the
+// vector-memory counter down before each such MFMA on every tile -- a
+// counter that by then also covers the next tile's copies, whose latency
+// those waits would expose.
+__device__ __forceinline__ void wait_vmem_known() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(size_t)(__attribute__((address_space(3))) const unsigned char*)p;
@@ -425,6 +434,7 @@ __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __
     }
     if (qt + 1 < n_qt) publish_lse(s ^ 1);
   };
+  wait_vmem_known();  // K^T, V^T (and the first tile's copies) have landed
   for (int qt = qt_first; qt < n_qt; qt += 2) {
     tile(std::integral_constant<int, 0>{}, qt);
     if (qt + 1 < n_qt) tile(std::integral_constant<int, 1>{}, qt + 1);
@@ -620,6 +630,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       block(std::false_type{}, 1);
     }
   };
+  wait_vmem_known();  // Q^T, dO^T (and the first tile's copies) have landed
   for (int kt = 0; kt < n_kt; kt += 2) {
     tile(std::integral_constant<int, 0>{}, kt);
     if (kt + 1 < n_kt) tile(std::integral_constant<int, 1>{}, kt + 1);
