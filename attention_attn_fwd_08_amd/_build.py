@@ -14,6 +14,10 @@ LIBRARY = os.path.join(PKG, "libattn_fwd.so")
 # Debug build of the forward alone: LDS filled with NaN before any copy
 # lands (tests compare it bit for bit with the library).
 POISON_LIBRARY = os.path.join(PKG, "libattn_fwd_lds_poison.so")
+# Debug build of the forward alone: every key tile takes the online-softmax
+# rescale branch (new maximum, O and l rescaled, probabilities formed again),
+# which ordinary inputs reach rarely; tests compare it with the oracle.
+RESCALE_LIBRARY = os.path.join(PKG, "libattn_fwd_force_rescale.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 instructions are switched off for all device code.
@@ -25,10 +29,16 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Build libattn_fwd.so (and the LDS-poison debug build of the forward)
-    in the package directory; returns the library's path."""
-    _compile(LIBRARY, list(SOURCES), [], verbose)
-    _compile(POISON_LIBRARY, [SOURCE], ["-DATTN_DEBUG_POISON_LDS"], verbose)
+    """Build libattn_fwd.so (and the two debug builds of the forward: LDS
+    poison, forced rescale) in the package directory, the three compiles in
+    parallel; returns the library's path."""
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = [(LIBRARY, list(SOURCES), []),
+            (POISON_LIBRARY, [SOURCE], ["-DATTN_DEBUG_POISON_LDS"]),
+            (RESCALE_LIBRARY, [SOURCE], ["-DATTN_DEBUG_FORCE_RESCALE"])]
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        for f in [ex.submit(_compile, out, srcs, extra, verbose) for out, srcs, extra in jobs]:
+            f.result()
     return LIBRARY
 
 

@@ -97,7 +97,7 @@ constexpr int kXcds = 8;
 // relative precision (and far from overflow).  Beyond it (or NaN / inf), the
 // tile's exact maximum becomes the reference, O and l are rescaled, and the
 // tile's probabilities are formed again.
-constexpr float kProbSumCap = 18446744073709551616.0f;
+[[maybe_unused]] constexpr float kProbSumCap = 18446744073709551616.0f;
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -600,11 +600,17 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       // becomes the reference (lanes L and L^32 agree on it), O and l are
       // rescaled and the probabilities formed again.  A row that has seen no
       // key until now (m = -inf, general shapes) takes its first finite m here.
+#ifdef ATTN_DEBUG_FORCE_RESCALE
+      const bool redo = true;  // debug build: every tile takes the rescale branch
+#else
       bool redo = !(l_tile <= kProbSumCap);
       if constexpr (GENERAL) redo = redo || (m_ref == -INFINITY && l_tile > 0.f);
+#endif
       if (__builtin_amdgcn_ballot_w64(redo)) {
         const float m_new = fmaxf(m_ref, tile_max(s_cur));
-        const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+        // A lane whose row has seen no key keeps m = -inf (its O and l are 0
+        // and stay 0): its factor is 1, not exp2(-inf - -inf) = NaN.
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
         l_run *= alpha;
 #pragma unroll
         for (int b = 0; b < kDBlocks; ++b)

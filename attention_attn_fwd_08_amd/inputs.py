@@ -120,6 +120,25 @@ def make_qkv_dout(B: int, H: int, N: int, d: int, seed: int,
     return tuple(out)
 
 
+def make_stepped_qkv(B: int, H: int, Nq: int, Nk: int, d: int, seed: int,
+                     q_shift: float, k_step: float, span: int, levels: int):
+    """Seeded bf16 Q [B,H,Nq,d], K and V [B,H,Nk,d] whose scores rise in steps
+    along the keys: every element of Q is offset by ``q_shift``, and every
+    element of key row j by ``k_step * min(j // span, levels - 1)`` (key
+    "level"), on top of standard normal samples (Q, then K, then V from one
+    PCG64 generator, rounded to bf16 like :func:`make_qkv`).  A query's score
+    against a key then grows by about ``q_shift * k_step * d`` per level, so
+    keys of a higher level dominate every key below it by a wide margin."""
+    rng = np.random.default_rng(seed)
+    zq = rng.standard_normal((B, H, Nq, d), dtype=np.float32)
+    zk = rng.standard_normal((B, H, Nk, d), dtype=np.float32)
+    zv = rng.standard_normal((B, H, Nk, d), dtype=np.float32)
+    level = np.minimum(np.arange(Nk) // span, levels - 1).astype(np.float32)
+    q = zq + np.float32(q_shift)
+    k = zk + (np.float32(k_step) * level)[None, None, :, None]
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(zv)
+
+
 def workload_inputs(w: Workload):
     """Seeded bf16 Q, K, V for a named workload."""
     return make_qkv(w.B, w.H, w.N, w.d, w.seed, w.qk_sigma, w.v_sigma)
@@ -134,13 +153,14 @@ def sample_rows(w: Workload, per_head: int = 16, block: int = 128, seed: int = 0
     """Flat row indices (b*H + h)*N + i to check at full size.
 
     Every head contributes the fixed rows 0, 1, block-1, block, N/2, N-1, the
-    last row before and the first row of each of two other query blocks, and
-    seeded random rows up to ``per_head``.
+    last row before and the first row of each of two other query blocks, the
+    same edges of 256-row blocks (255, 256, 511, 512), and seeded random rows
+    up to ``per_head``.
     """
     rng = np.random.default_rng(1000 + seed)
     N = w.N
     fixed = {0, 1, block - 1, block, N // 2, N - 1, min(N - 1, 2 * block - 1),
-             min(N - 1, 3 * block)}
+             min(N - 1, 3 * block), 255, 256, 511, 512}
     fixed = sorted(r for r in fixed if 0 <= r < N)
     rows = []
     for bh in range(w.B * w.H):

@@ -1,7 +1,9 @@
 """GPU parity at the head dims beyond 64 and 128 (32, 96 and 256) against the
 fp64 oracles, for the three forward entry points, at the forward's
-tolerances: several query and key tiles, ragged tails, causal and not, and a
-sharp-score case (q, k with sigma 2) that exercises the rescale path."""
+tolerances: several query and key tiles, ragged tails, causal and not, and
+sharper scores (q, k with sigma 2).  Those stay far below the kernel's
+rescale threshold; the rescale branch itself is run by the planted-score and
+forced-rescale tests in test_rescale_gpu.py."""
 import math
 
 import numpy as np

@@ -82,7 +82,8 @@ def test_workload_sampled(name):
     log(f"[workload sampled] {name}")
     q, k, v = workload_inputs(w)
     o, lse = run_gpu(q, k, v, w.causal, w.scale)
-    rows = sample_rows(w)
+    # fixed rows at the edges of the kernel's query tiles (256 queries at d=128)
+    rows = sample_rows(w, block=256 if w.d == 128 else 128)
     o_ref, lse_ref = oracle.attention_rows(q, k, v, w.causal, w.scale, rows,
                                            threads=ORACLE_THREADS)
     o_g = to_host_f64(o.reshape(-1, w.d)[rows])
