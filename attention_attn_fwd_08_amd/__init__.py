@@ -28,7 +28,8 @@ import os
 import threading
 
 __all__ = ["attn_fwd", "attn_fwd_raw", "attn_fwd_ex", "attn_fwd_ex_raw", "attn_fwd_splitkv",
-           "attn_fwd_splitkv_raw", "splitkv_splits", "attn_bwd",
+           "attn_fwd_splitkv_raw", "attn_fwd_splitkv_noalloc", "attn_fwd_splitkv_noalloc_raw",
+           "splitkv_splits", "attn_bwd",
            "attn_bwd_raw", "attn_bwd_ex", "attn_bwd_ex_raw", "gemm", "gemm_raw", "GEMM_NN", "GEMM_NT", "attn_fwd_strerror",
            "load_library", "LIBRARY", "Status", "AttnError"]
 
@@ -50,6 +51,7 @@ class Status:
     ERR_SCALE = 6
     ERR_HIP = 7
     ERR_DEVICE = 8
+    ERR_WORKSPACE = 9
 
 
 class AttnError(RuntimeError):
@@ -89,6 +91,9 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.attn_fwd_splitkv.argtypes = ([vp] * 5 + [ctypes.c_int] * 6 + [ctypes.c_float, ctypes.c_int]
                                      + [vp] * 3)
     lib.attn_fwd_splitkv.restype = ctypes.c_int
+    lib.attn_fwd_splitkv_noalloc.argtypes = ([vp] * 5 + [ctypes.c_int] * 6
+                                             + [ctypes.c_float, ctypes.c_int, vp])
+    lib.attn_fwd_splitkv_noalloc.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [vp] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float, vp]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd_ex.argtypes = [vp] * 10 + [ctypes.c_int] * 6 + [ctypes.c_float, vp]
@@ -379,6 +384,51 @@ def attn_fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
         status = attn_fwd_splitkv_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                       lse.data_ptr(), B, H, Nq, Nk, d, causal, scale, n_splits,
                                       o_part.data_ptr(), lse_part.data_ptr(), stream)
+    if status != Status.OK:
+        raise AttnError(status, attn_fwd_strerror(status))
+    return out, lse
+
+
+def attn_fwd_splitkv_noalloc_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
+                                 B: int, H: int, Nq: int, Nk: int, d: int, causal: bool,
+                                 scale: float, n_splits: int, stream: int = 0) -> int:
+    """Call attn_fwd_splitkv_noalloc with raw integer addresses; returns the status."""
+    lib = load_library()
+    return lib.attn_fwd_splitkv_noalloc(q_ptr or None, k_ptr or None, v_ptr or None,
+                                        o_ptr or None, lse_ptr or None, int(B), int(H), int(Nq),
+                                        int(Nk), int(d), int(bool(causal)), float(scale),
+                                        int(n_splits), stream or None)
+
+
+def attn_fwd_splitkv_noalloc(q, k, v, causal: bool = False, scale: float | None = None,
+                             n_splits: int | None = None, out=None, lse=None):
+    """:func:`attn_fwd_splitkv` with its partial results in the library's fixed
+    device workspace instead of caller tensors (the library allocates nothing;
+    calls that overlap in time on one GPU race).  With ``out`` and ``lse``
+    given, this call allocates nothing either."""
+    import torch
+
+    _check_bf16("q", q, None, None)
+    B, H, Nq, d = q.shape
+    _check_bf16("k", k, None, q.device)
+    if k.shape[:2] != (B, H) or k.shape[3] != d:
+        raise ValueError("k must be [B, H, Nk, d] with q's B, H and d")
+    _check_bf16("v", v, k.shape, q.device)
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if n_splits is None:
+        n_splits = splitkv_splits(B, H, Nq, Nk, d)
+    out = torch.empty_like(q) if out is None else out
+    _check_bf16("out", out, q.shape, q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_f32("lse", lse, (B, H, Nq), q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        status = attn_fwd_splitkv_noalloc_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                              out.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
+                                              causal, scale, n_splits, stream)
     if status != Status.OK:
         raise AttnError(status, attn_fwd_strerror(status))
     return out, lse

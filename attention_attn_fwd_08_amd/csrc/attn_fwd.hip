@@ -907,6 +907,72 @@ int check_device() {
   return ATTN_OK;
 }
 
+// The split-KV forward with its partial results in o_part / lse_part
+// (caller workspace, or the fixed device workspace below); `used` ranges of
+// `chunk` keys, computed by the caller from the request.
+int splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+            int Nk, int d, int causal, float scale, int used, int chunk, float* o_part,
+            float* lse_part, hipStream_t s) {
+  if (used <= 1)  // nothing to split (or no key at all)
+    return dispatch<true>(q, k, v, o, lse, B * H, Nq, Nk, d, causal, scale, s);
+  const float c = scale * kLog2e;
+  const int off = causal ? Nk - Nq : 0;
+  const int BH = B * H;
+  auto go = [&](auto d_tag) {
+    constexpr int D = decltype(d_tag)::value;
+    return causal
+               ? launch_split<D, true>(q, k, v, o, lse, BH, Nq, Nk, off, c, used, chunk, o_part, lse_part, s)
+               : launch_split<D, false>(q, k, v, o, lse, BH, Nq, Nk, off, c, used, chunk, o_part, lse_part, s);
+  };
+  switch (d) {
+    case 32: return go(std::integral_constant<int, 32>{});
+    case 64: return go(std::integral_constant<int, 64>{});
+    case 96: return go(std::integral_constant<int, 96>{});
+    case 128: return go(std::integral_constant<int, 128>{});
+    default: return go(std::integral_constant<int, 256>{});
+  }
+}
+
+// Split-KV argument checks shared by both split entry points (before any HIP
+// call): ranges of whole 64-key tiles, `used` of them.
+int check_split(int B, int H, int Nq, int Nk, int d, int n_splits, int* chunk, int* used) {
+  if (n_splits < 1) return ATTN_ERR_SHAPE;
+  const int64_t chunk64 = ((int64_t)Nk + n_splits - 1) / n_splits;
+  *chunk = (int)(((chunk64 + 63) / 64) * 64);
+  *used = Nk > 0 ? (int)(((int64_t)Nk + *chunk - 1) / *chunk) : 0;
+  if (*used > 65535) return ATTN_ERR_SHAPE;
+  if ((int64_t)*used * B * H * Nq * d > ((int64_t)1 << 40)) return ATTN_ERR_SHAPE;
+  return ATTN_OK;
+}
+
+constexpr size_t kScratchBytes = size_t(32) << 20;
+
+}  // namespace
+
+// Fixed device workspace of attn_fwd_splitkv_noalloc: the fp32 partial O of
+// every split, then (from a 256-byte boundary) the partial LSE.  One copy per
+// GPU, for the life of the process.  Host code never passes this symbol to a
+// kernel (on the host it names a stand-in, not device memory): it uses the
+// device address looked up once per device by scratch_on().
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on device `dev` (the current device), or null
+// if the runtime cannot give it.
+void* scratch_on(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) ptr = nullptr;
+    g_scratch_ptr[dev] = ptr;
+  });
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -936,36 +1002,42 @@ extern "C" int attn_fwd_splitkv(const void* q, const void* k, const void* v, voi
   bool nothing = false;
   int st = check_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, &nothing);
   if (st != ATTN_OK) return st;
-  if (n_splits < 1) return ATTN_ERR_SHAPE;
+  int chunk = 0, used = 0;
+  if ((st = check_split(B, H, Nq, Nk, d, n_splits, &chunk, &used)) != ATTN_OK) return st;
   if (nothing) return ATTN_OK;
-  // Splits of whole 64-key tiles; the grid's second dimension counts them.
-  const int64_t chunk64 = ((int64_t)Nk + n_splits - 1) / n_splits;
-  const int chunk = (int)(((chunk64 + 63) / 64) * 64);
-  const int used = Nk > 0 ? (int)(((int64_t)Nk + chunk - 1) / chunk) : 0;
-  if (used > 65535) return ATTN_ERR_SHAPE;
-  if ((int64_t)used * B * H * Nq * d > ((int64_t)1 << 40)) return ATTN_ERR_SHAPE;
-  if (used > 0 && (!o_part || !lse_part)) return ATTN_ERR_NULL;
+  if (used > 1 && (!o_part || !lse_part)) return ATTN_ERR_NULL;
   if (!aligned16(o_part) || !aligned16(lse_part)) return ATTN_ERR_ALIGN;
   if ((st = check_device()) != ATTN_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (used <= 1)  // nothing to split (or no key at all)
-    return dispatch<true>(q, k, v, o, lse, B * H, Nq, Nk, d, causal, scale, s);
-  const float c = scale * kLog2e;
-  const int off = causal ? Nk - Nq : 0;
-  const int BH = B * H;
-  auto go = [&](auto d_tag) {
-    constexpr int D = decltype(d_tag)::value;
-    return causal
-               ? launch_split<D, true>(q, k, v, o, lse, BH, Nq, Nk, off, c, used, chunk, o_part, lse_part, s)
-               : launch_split<D, false>(q, k, v, o, lse, BH, Nq, Nk, off, c, used, chunk, o_part, lse_part, s);
-  };
-  switch (d) {
-    case 32: return go(std::integral_constant<int, 32>{});
-    case 64: return go(std::integral_constant<int, 64>{});
-    case 96: return go(std::integral_constant<int, 96>{});
-    case 128: return go(std::integral_constant<int, 128>{});
-    default: return go(std::integral_constant<int, 256>{});
+  return splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, used, chunk, o_part, lse_part,
+                 static_cast<hipStream_t>(stream));
+}
+
+extern "C" int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
+                                        float* lse, int B, int H, int Nq, int Nk, int d,
+                                        int causal, float scale, int n_splits, void* stream) {
+  bool nothing = false;
+  int st = check_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, &nothing);
+  if (st != ATTN_OK) return st;
+  int chunk = 0, used = 0;
+  if ((st = check_split(B, H, Nq, Nk, d, n_splits, &chunk, &used)) != ATTN_OK) return st;
+  if (nothing) return ATTN_OK;
+  // Partial O, then the partial LSE from a 256-byte boundary, in the fixed workspace.
+  const size_t rows = (size_t)used * B * H * Nq;
+  const size_t o_bytes = (rows * d * sizeof(float) + 255) & ~(size_t)255;
+  if (used > 1 && o_bytes + rows * sizeof(float) > kScratchBytes) return ATTN_ERR_WORKSPACE;
+  if ((st = check_device()) != ATTN_OK) return st;
+  float* o_part = nullptr;
+  float* lse_part = nullptr;
+  if (used > 1) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+    unsigned char* base = static_cast<unsigned char*>(scratch_on(dev));
+    if (!base) return ATTN_ERR_HIP;
+    o_part = reinterpret_cast<float*>(base);
+    lse_part = reinterpret_cast<float*>(base + o_bytes);
   }
+  return splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, used, chunk, o_part, lse_part,
+                 static_cast<hipStream_t>(stream));
 }
 
 extern "C" const char* attn_fwd_strerror(int status) {
@@ -979,8 +1051,9 @@ extern "C" const char* attn_fwd_strerror(int status) {
     case ATTN_ERR_SCALE: return "scale must be finite and greater than 0";
     case ATTN_ERR_HIP: return "the HIP runtime reported an error";
     case ATTN_ERR_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
+    case ATTN_ERR_WORKSPACE: return "the partial results exceed the library's fixed 32 MiB workspace";
     default: return "unknown status";
   }
 }
 
-extern "C" int attn_fwd_abi_version(void) { return 3; }
+extern "C" int attn_fwd_abi_version(void) { return 4; }

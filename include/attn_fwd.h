@@ -41,7 +41,9 @@ enum attn_fwd_status {
     ATTN_ERR_ALIGN = 5,        /* a pointer is not 16-byte aligned             */
     ATTN_ERR_SCALE = 6,        /* scale is not finite or not > 0               */
     ATTN_ERR_HIP = 7,          /* the HIP runtime reported an error at launch  */
-    ATTN_ERR_DEVICE = 8        /* the current device is not a gfx950 GPU       */
+    ATTN_ERR_DEVICE = 8,       /* the current device is not a gfx950 GPU       */
+    ATTN_ERR_WORKSPACE = 9     /* attn_fwd_splitkv_noalloc: partial results
+                                  larger than its fixed workspace              */
 };
 
 /*
@@ -131,11 +133,38 @@ int attn_fwd_splitkv(const void *q, const void *k, const void *v,
                      int n_splits, float *o_part, float *lse_part,
                      void *stream);
 
+/*
+ * attn_fwd_splitkv_noalloc -- attn_fwd_splitkv without the workspace
+ * arguments, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The partial results live in a fixed 32 MiB array of device memory inside
+ * the library (one per GPU, held until the process ends): fp32 partial O
+ * [n_used, B, H, Nq, d], then, from the next 256-byte boundary, the partial
+ * LSE [n_used, B, H, Nq], with n_used as for attn_fwd_splitkv.  A problem
+ * whose partial results do not fit returns ATTN_ERR_WORKSPACE before any HIP
+ * call.  The call allocates nothing: the first call on a device looks up the
+ * array's device address once.  Every call on one GPU shares that array, so
+ * calls that overlap in time on one GPU (different streams or host threads
+ * without ordering between them) race and give undefined results; calls
+ * ordered on one stream are safe.  Every partial result is written before it
+ * is read in the same call, so nothing needs clearing between calls.
+ *
+ * Every other argument, and the result, errors and semantics, are as for
+ * attn_fwd_splitkv (results are identical to it for the same n_splits).
+ */
+int attn_fwd_splitkv_noalloc(const void *q, const void *k, const void *v,
+                             void *o, float *lse,
+                             int B, int H, int Nq, int Nk, int d,
+                             int causal, float scale, int n_splits,
+                             void *stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *attn_fwd_strerror(int status);
 
-/* ABI version of this header's entry points (currently 3: attn_fwd_ex and
- * attn_fwd_splitkv added to version 1). */
+/* ABI version of this header's entry points (currently 4: attn_fwd_ex and
+ * attn_fwd_splitkv added to version 1 in 3, attn_fwd_splitkv_noalloc and
+ * ATTN_ERR_WORKSPACE in 4). */
 int attn_fwd_abi_version(void);
 
 #ifdef __cplusplus

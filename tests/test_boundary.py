@@ -40,8 +40,8 @@ def declared_functions():
 def test_headers_declare_the_entry_points():
     assert [os.path.basename(h) for h in HEADERS] == ["attn_bwd.h", "attn_fwd.h", "attn_gemm.h"]
     assert declared_functions() == ["attn_bwd", "attn_bwd_ex", "attn_fwd", "attn_fwd_abi_version",
-                                    "attn_fwd_ex", "attn_fwd_splitkv", "attn_fwd_strerror",
-                                    "attn_gemm_bf16"]
+                                    "attn_fwd_ex", "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc",
+                                    "attn_fwd_strerror", "attn_gemm_bf16"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -58,7 +58,7 @@ def test_status_codes_match_header(lib):
         msg = af.attn_fwd_strerror(value)
         assert msg and msg != "unknown status"
     assert af.attn_fwd_strerror(12345) == "unknown status"
-    assert lib.attn_fwd_abi_version() == 3
+    assert lib.attn_fwd_abi_version() == 4
 
 
 def call(B=2, H=3, N=256, d=128, causal=0, scale=0.088, q=FAKE, k=FAKE, v=FAKE, o=FAKE,
@@ -225,6 +225,32 @@ def test_splitkv_rejects(lib, kw, status):
 @pytest.mark.parametrize("kw", [dict(Nq=0), dict(H=0), dict(Nq=0, o_part=0, lse_part=0)])
 def test_splitkv_empty_problem_is_a_noop(lib, kw):
     assert call_split(**kw) == af.Status.OK
+
+
+def call_noalloc(B=2, H=3, Nq=1, Nk=4096, d=128, causal=0, scale=0.088, n_splits=16, q=FAKE,
+                 k=FAKE, v=FAKE, o=FAKE, lse=FAKE):
+    return af.attn_fwd_splitkv_noalloc_raw(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, n_splits)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_splits=0), af.Status.ERR_SHAPE),
+    (dict(Nk=-1), af.Status.ERR_SHAPE),
+    (dict(d=160), af.Status.ERR_HEAD_DIM),
+    (dict(q=0), af.Status.ERR_NULL),
+    (dict(lse=FAKE + 8), af.Status.ERR_ALIGN),
+    (dict(scale=0.0), af.Status.ERR_SCALE),
+    (dict(Nk=1 << 22, n_splits=1 << 16), af.Status.ERR_SHAPE),
+    # partial results past the fixed 32 MiB workspace (checked before any HIP call)
+    (dict(B=1, H=64, Nq=512, Nk=65536, n_splits=4), af.Status.ERR_WORKSPACE),
+    (dict(B=1, H=1, Nq=1, Nk=1 << 21, d=256, n_splits=40000), af.Status.ERR_WORKSPACE),
+])
+def test_noalloc_rejects(lib, kw, status):
+    assert call_noalloc(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(Nq=0), dict(H=0), dict(B=0, q=0, k=0, v=0, o=0, lse=0)])
+def test_noalloc_empty_problem_is_a_noop(lib, kw):
+    assert call_noalloc(**kw) == af.Status.OK
 
 
 def test_splitkv_split_choice():
