@@ -595,6 +595,14 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         }
       };
       probs();
+      // The bf16 probabilities are formed here, before the rescale test, so
+      // their conversions interleave with the exponentials instead of
+      // waiting for the branch (measured 1 % faster at d=128, 1.6 % at d=64;
+      // the common path's results are unchanged).
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) asm volatile("" : "+v"(pb[sb][cc]));
       // Lazy rescale, checked on the probabilities themselves (the lane's tile
       // sum; NaN and inf fail the test too).  Rare: the tile's exact maximum
       // becomes the reference (lanes L and L^32 agree on it), O and l are

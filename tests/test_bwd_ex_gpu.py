@@ -25,6 +25,8 @@ SHAPES = [
     (1, 1, 513, 257, 64, False), (1, 2, 200, 450, 64, True),
     (1, 1, 77, 33, 128, True), (1, 2, 100, 300, 32, True), (1, 2, 300, 130, 96, True),
     (1, 1, 64, 500, 96, False), (1, 2, 100, 300, 256, True), (1, 1, 300, 130, 256, True),
+    # at least one key block per CU at d=128: the 8-wave dK/dV workgroups
+    (1, 80, 300, 700, 128, True), (1, 128, 700, 256, 128, True), (2, 64, 200, 500, 128, False),
 ]
 
 
