@@ -18,6 +18,10 @@ POISON_LIBRARY = os.path.join(PKG, "libattn_fwd_lds_poison.so")
 # rescale branch (new maximum, O and l rescaled, probabilities formed again),
 # which ordinary inputs reach rarely; tests compare it with the oracle.
 RESCALE_LIBRARY = os.path.join(PKG, "libattn_fwd_force_rescale.so")
+# Test library: the forward's layout functions run on one tile, returning
+# every fragment (the layout tests check them against host matrices).
+LAYOUT_SOURCE = os.path.join(PKG, "csrc", "layout_probe.hip")
+LAYOUT_LIBRARY = os.path.join(PKG, "liblayout_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 instructions are switched off for all device code.
@@ -29,13 +33,14 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Build libattn_fwd.so (and the two debug builds of the forward: LDS
-    poison, forced rescale) in the package directory, the three compiles in
-    parallel; returns the library's path."""
+    """Build libattn_fwd.so, the two debug builds of the forward (LDS
+    poison, forced rescale) and the layout-probe test library in the package
+    directory, the compiles in parallel; returns the library's path."""
     from concurrent.futures import ThreadPoolExecutor
     jobs = [(LIBRARY, list(SOURCES), []),
             (POISON_LIBRARY, [SOURCE], ["-DATTN_DEBUG_POISON_LDS"]),
-            (RESCALE_LIBRARY, [SOURCE], ["-DATTN_DEBUG_FORCE_RESCALE"])]
+            (RESCALE_LIBRARY, [SOURCE], ["-DATTN_DEBUG_FORCE_RESCALE"]),
+            (LAYOUT_LIBRARY, [LAYOUT_SOURCE], [])]
     with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         for f in [ex.submit(_compile, out, srcs, extra, verbose) for out, srcs, extra in jobs]:
             f.result()

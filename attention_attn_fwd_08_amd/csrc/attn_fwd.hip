@@ -63,19 +63,10 @@
 #include <type_traits>
 
 #include "attn_fwd.h"
+#include "fwd_tile_layout.h"
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-constexpr int kWave = 64;
-constexpr int kQueriesPerWave = 32;
 // Waves per workgroup: d=128 runs one 8-wave workgroup per CU (two waves per
 // SIMD; each K/V tile is fetched into LDS once per 256 queries); d=32, 64 and
 // 96 run 4-wave workgroups, two or more per CU; d=256 runs one 4-wave
@@ -89,7 +80,6 @@ struct Launch {
   static constexpr int kBlockM = kWaves * kQueriesPerWave;  // queries per workgroup
   static constexpr int kMinBlocks = (D == 128 || D == 256) ? 1 : 2;  // launch-bounds occupancy hint
 };
-constexpr int kBlockN = 64;                        // keys per LDS stage
 constexpr int kXcds = 8;
 // Probabilities are formed against a stale reference maximum for as long as
 // a lane's sum over one tile stays at or below this (2^64): each is then at
@@ -102,89 +92,6 @@ constexpr int kXcds = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
-// LDS layouts.  A K or V stage is kBlockN rows of D bf16 (D*2 bytes); the
-// 16-byte chunks of each row are permuted by an XOR with a function of the
-// row, chosen against the way gfx950 services each read (measured with the
-// LDS bank-conflict counter: 16-byte reads are serviced 16 lanes at a time,
-// the 8-byte transposed reads 32 lanes at a time, 256 bytes per pass).
-//
-// K is read as the MFMA A operand: 16 lanes read the same chunk of 16
-// consecutive rows.  d=128 and d=256 (rows a multiple of 256 bytes): XOR with
-// row%16 puts them in 16 distinct chunk positions.  d=64 (128-byte rows, two
-// rows per 256-byte pass): the 8 even and the 8 odd rows of the 16 each land
-// in distinct chunks.  d=32 and d=96 (row stride 4 or 12 chunks, so rows
-// r, r+4, r+8, r+12 share a bank group and the four residues of r mod 4 use
-// disjoint ones): XOR with (row/4)%4 separates the four rows of a residue
-// inside their group of four chunks (and keeps a chunk below D/8).
-//
-// V is read with ds_read_b64_tr_b16: 32 lanes read 4 consecutive rows x 2
-// adjacent 32-byte chunk pairs; the XOR moves the pair index by 2*(row%4) (+1
-// every 4 rows), so the 8 (row, pair) reads cover 8 distinct pair positions.
-// d=64: the two even (and two odd) rows of the 4 get pair offsets 0 and 2.
-// d=32 (the 4 rows are 256 contiguous bytes) and d=96 (row offsets 0, 192,
-// 384, 576 fall in 4 distinct 64-byte bank quarters) need no swizzle.
-template <int D>
-__device__ __forceinline__ int k_swz(int row) {
-  if constexpr (D == 128 || D == 256) return row & 15;
-  else if constexpr (D == 64) return (row & 7) ^ ((row >> 3) & 1);
-  else return (row >> 2) & 3;
-}
-template <int D>
-__device__ __forceinline__ int v_swz(int row) {
-  if constexpr (D == 128 || D == 256) return 4 * (row & 3) + 2 * ((row >> 2) & 1);
-  else if constexpr (D == 64) return 4 * ((row >> 1) & 1);
-  else return 0;
-}
-// Byte offset of 32-feature block b of a V row read at `off` (block 0): with
-// rows a multiple of 128 bytes the block index is chunk bits 2.. of the
-// swizzled offset (XOR, which composes with the swizzle); d=96 rows are not,
-// and are unswizzled, so the block is a plain displacement.
-template <int D>
-__device__ __forceinline__ int v_block(int off, int b) {
-  if constexpr (D == 96) return off + 64 * b;
-  else return off ^ (b << 6);
-}
-
-// 16 bytes global -> LDS without passing through registers, through a buffer
-// resource {base, byte size}: lane i of the wave reads bytes [voff, voff+16)
-// of the buffer (offsets past the size, which the hardware range-checks,
-// return zeros) and
-// writes them to LDS bytes [16i, 16i+16) after the wave-uniform LDS byte
-// address `lds_addr` (set through M0).  Issued as inline assembly so the compiler does
-// not wait for these loads before unrelated LDS reads; the kernel waits for
-// them itself (wait_lds_dma) before the barrier that publishes them.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
-  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
-  // Word 3 = 0x00020000: raw (untyped) 32-bit data for gfx9-family buffers.
-  return i32x4{(int)(unsigned)a, (int)((unsigned)(a >> 32) & 0xffffu), bytes, 0x00020000};
-}
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// The LDS address is `lds_addr + OFF`, OFF a compile-time byte offset added
-// inside the asm, so only the base occupies a scalar register.
-template <unsigned OFF>
-__device__ __forceinline__ void load16_to_lds(i32x4 rsrc, int voff, unsigned lds_addr) {
-  asm volatile("s_add_u32 m0, %2, %3\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(lds_addr), "n"(OFF)
-               : "memory", "m0", "scc");
-}
-#pragma clang diagnostic pop
-// f(integral_constant<int, I>) for I = B .. E-1.
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
-// Wait until at most N of this wave's LDS-bound loads are still in flight.
-template <int N>
-__device__ __forceinline__ void wait_lds_dma() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // max / sum of a value held by lanes L and L^32 (the two halves of one query).
 __device__ __forceinline__ float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
@@ -195,52 +102,6 @@ __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                                   false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Per-wave state and the steps of one 64-key tile.  The tile loop is software
-// pipelined: while the scores of tile t are turned into probabilities (VALU,
-// transcendental) the MFMA pipe computes the scores of tile t+1, and then
-// O^T += V_t^T P_t^T runs on the MFMA pipe (with the mask of tile t+1 on the
-// VALU when it needs one).  K therefore runs one tile ahead of V.
-template <int D>
-struct Tile {
-  static constexpr int kRowBytes = D * 2;
-  static constexpr int kSteps = D / 16;    // MFMA k-steps of one 32x32 score block
-  static constexpr int kDBlocks = D / 32;  // 32-row blocks of O^T
-  static constexpr int kStageBytes = kBlockN * kRowBytes;
-};
-
-// Scores S^T of one 32-key block (sb) of a K stage against this wave's 32
-// queries.
-template <int D>
-__device__ __forceinline__ void scores_block(const unsigned char* k_lds, int sb,
-                                             const int (&k_off)[Tile<D>::kSteps],
-                                             const bf16x8 (&qf)[Tile<D>::kSteps], f32x16& s) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-  for (int st = 0; st < Tile<D>::kSteps; ++st) {
-    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(k_lds + sb * 32 * Tile<D>::kRowBytes + k_off[st]);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s, 0, 0, 0);
-  }
-}
-
-// Scores S^T of the two 32-key blocks of a K stage against this wave's 32
-// queries.  Accumulator register r of lane L: key 8*(r/4) + 4*(L/32) + r%4 of
-// the block, query L%32.
-template <int D>
-__device__ __forceinline__ void scores(const unsigned char* k_lds, const int (&k_off)[Tile<D>::kSteps],
-                                       const bf16x8 (&qf)[Tile<D>::kSteps], f32x16 (&s)[2]) {
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-#pragma unroll
-    for (int st = 0; st < Tile<D>::kSteps; ++st) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(k_lds + sb * 32 * Tile<D>::kRowBytes + k_off[st]);
-      s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[sb], 0, 0, 0);
-    }
-  }
 }
 
 // Mask of a tile whose keys start at key0 for the queries q0 + L%32: a key is
@@ -300,7 +161,6 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int off = GENERAL ? off_arg - kv_begin : 0;
   using T = Tile<D>;
   constexpr int kRowBytes = T::kRowBytes;
-  constexpr int kChunksPerRow = D / 8;
   constexpr int kSteps = T::kSteps;
   constexpr int kDBlocks = T::kDBlocks;
   constexpr int kStageBytes = T::kStageBytes;
@@ -351,19 +211,16 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     if (grid % kXcds == 0) lid = (lid % kXcds) * (grid / kXcds) + lid / kXcds;
   }
 
-  // Global -> LDS copy of one K or V tile.  The stage is a row-major array of
-  // 16-byte chunks; lane i of wave load w fills chunk g = 64w + i (bytes
-  // [16g, 16g+16)): row g/kChunksPerRow, physical chunk g%kChunksPerRow,
-  // which holds logical chunk (that ^ swz).  The buffer starts at the tile,
-  // so rows past the keys fall outside its size.
+  // Global -> LDS copy of one K or V tile: lane i of wave load w fills LDS
+  // chunk g = 64w + i of the stage from the tile offset k_copy_offset /
+  // v_copy_offset (the swizzled layout).  The buffer starts at the tile, so
+  // rows past the keys fall outside its size.
   int k_ld_off[kLoadsPerWave], v_ld_off[kLoadsPerWave];
 #pragma unroll
   for (int it = 0; it < kLoadsPerWave; ++it) {
     const unsigned g = (wave * kLoadsPerWave + it) * kWave + lane;
-    const int row = (int)(g / kChunksPerRow);
-    const int chunk = (int)(g % kChunksPerRow);
-    k_ld_off[it] = row * kRowBytes + ((chunk ^ k_swz<D>(row)) << 4);
-    v_ld_off[it] = row * kRowBytes + ((chunk ^ v_swz<D>(row)) << 4);
+    k_ld_off[it] = k_copy_offset<D>(g);
+    v_ld_off[it] = v_copy_offset<D>(g);
   }
   const unsigned lds_wave = (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char*)smem +
                             wave * kLoadsPerWave * kLoadBytes;
@@ -380,36 +237,23 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   using kRegionK = std::integral_constant<int, 0>;
   using kRegionV = std::integral_constant<int, 1>;
 
-  // Per-lane LDS byte offsets (stage-relative) of the operand reads.
-  // K (A operand of S^T): row L%32 (+32 per block), logical chunk 2*st + L/32.
+  // Per-lane LDS byte offsets (stage-relative) of the operand reads: K at
+  // row L%32, features 16*st + 8*(L/32) ..; V transposed, so that lane L
+  // holds the keys of P^T's slots (fwd_tile_layout.h).
   int k_off[kSteps];
 #pragma unroll
-  for (int st = 0; st < kSteps; ++st)
-    k_off[st] = l32 * kRowBytes + (((2 * st + half) ^ k_swz<D>(l32)) << 4);
-  // V (A operand of O^T, transposed reads): 16-lane group G = L/16 and
-  // s = L%16 read row 16*cc + 4*(G/2) + s/4 (+8 for the second read) and
-  // features 32*b + 16*(G%2) + 4*(s%4) .. +3; lane L then holds feature
-  // 32*b + L%32 of keys 16cc + 4*(L/32) + 0..3 (first read) and
-  // 16cc + 8 + 4*(L/32) + 0..3 (second read), the key order of P^T's slots.
-  // The swizzle depends on row%16 only, identical for every (sb, cc), and the
-  // d-block b only flips bits 6-7 of the offset (chunk bits 2-3).
-  const int g16 = lane >> 4;
-  const int s16 = lane & 15;
+  for (int st = 0; st < kSteps; ++st) k_off[st] = k_operand_offset<D>(l32, half, st);
   int v_off[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int r = 4 * (g16 >> 1) + (s16 >> 2) + 8 * h;
-    const int col = 16 * (g16 & 1) + 4 * (s16 & 3);
-    v_off[h] = r * kRowBytes + (((col >> 3) ^ v_swz<D>(r)) << 4) + (col & 7) * 2;
-  }
+  for (int h = 0; h < 2; ++h) v_off[h] = v_operand_offset<D>(lane, h);
 
   // Number of key tiles a query tile visits (causal: up to its last query).
   auto tiles_of = [&](int qt) __attribute__((always_inline)) {
     const int kv_end = CAUSAL ? min((qt + 1) * kBlockM + off, Nk) : Nk;
     return (kv_end + kBlockN - 1) / kBlockN;
   };
-  // Q^T as MFMA B operand: lane L holds query q0+L%32, features 8*(L/32)..+7
-  // of each 16-feature step.  Loaded once per query tile.
+  // Q^T as MFMA B operand (q_operand): lane L holds query q0+L%32.  Loaded
+  // once per query tile.
   bf16x8 qf[kSteps];
   // Start of a query tile: its first K, V and second K tiles go to LDS and
   // its Q to registers.
@@ -423,9 +267,7 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     load_tile(v + kv_off_t, v_ld_off, kRegionV{}, 0, 0);
     if (nt > 1) load_tile(k + kv_off_t, k_ld_off, kRegionK{}, 1, 1);
     const int row = min(qt_t * kBlockM + wave * kQueriesPerWave + l32, N - 1);  // rows past N: any valid row
-    const __bf16* qrow = q + (size_t)head_t * N * D + (size_t)row * D + 8 * half;
-#pragma unroll
-    for (int st = 0; st < kSteps; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st);
+    q_operand<D>(q + (size_t)head_t * N * D + (size_t)row * D, half, qf);
   };
 #ifdef ATTN_DEBUG_POISON_LDS
   // Debug build: every LDS byte starts as a NaN pattern, so an operand read
@@ -642,10 +484,7 @@ void attn_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
         for (int b = 0; b < kDBlocks; ++b)
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc) {
-            const unsigned char* a = v_lds + (sb * 32 + cc * 16) * kRowBytes;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + v_block<D>(v_off[0], b)));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + v_block<D>(v_off[1], b)));
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            const bf16x8 vf = v_operand<D>(v_lds + (sb * 32 + cc * 16) * kRowBytes, v_off, b);
             acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[sb][cc], acc[b], 0, 0, 0);
           }
       }

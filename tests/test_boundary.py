@@ -50,6 +50,20 @@ def test_library_exports_every_declared_symbol(lib):
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
 
 
+def test_layout_probe_library_loads_and_rejects_bad_arguments(lib):
+    """The test library of the layout probes exports its two entry points,
+    which reject bad arguments before any HIP call."""
+    from attention_attn_fwd_08_amd import _build
+    probe = ctypes.CDLL(_build.LAYOUT_LIBRARY)
+    p = ctypes.c_void_p
+    probe.layout_probe_tile.argtypes = [ctypes.c_int, p, p, p, ctypes.c_int, p, p, p, p, p, p]
+    probe.layout_probe_mfma.argtypes = [p, p, p, p, p]
+    assert probe.layout_probe_tile(48, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert probe.layout_probe_tile(128, FAKE, FAKE, FAKE, 65, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert probe.layout_probe_tile(128, None, FAKE, FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert probe.layout_probe_mfma(FAKE, FAKE, None, FAKE, None) == 1
+
+
 def test_status_codes_match_header(lib):
     text = open(HEADER).read()
     codes = dict((n, int(v)) for n, v in re.findall(r"ATTN_(ERR_\w+|OK)\s*=\s*(\d+)", text))
