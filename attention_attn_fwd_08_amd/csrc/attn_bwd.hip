@@ -249,6 +249,12 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const __bf16* __restrict
 constexpr int kQT = 64;  // queries per streamed Q / dO tile
 template <int D>
 constexpr int dkdv_smem_bytes() { return 2 * (2 * kQT * D * 2 + 2 * kQT * 4); }  // 2 stages
+// The paired workgroup's P exchange (PART 3 / 4 below): per dV wave, per
+// 32-query block of the tile, the bf16 P of its 32 keys (16 values per lane,
+// two 16-byte chunks), behind the two stages.
+constexpr int kPShareBytes = kWaves * (kQT / kRows) * 2 * kWave * 16;
+template <int D>
+constexpr int dkdv_pair_smem_bytes() { return dkdv_smem_bytes<D>() + kPShareBytes; }
 
 // The work of one group of four waves on key block `lid` (head * blocks +
 // block).  PART 0: dK and dV together (d=64: several waves per SIMD fit).
@@ -257,12 +263,19 @@ constexpr int dkdv_smem_bytes() { return 2 * (2 * kQT * D * 2 + 2 * kQT * 4); } 
 // K, V and the scores in the registers of two waves per SIMD, so the parts
 // run in separate waves: S is formed twice, but every wave runs at two waves
 // per SIMD (measured: about 18 % less time than one combined wave per SIMD).
-// Both parts of a key block run in one 8-wave workgroup (NW = 8: the dV
-// waves 0-3 and the dK waves 4-7 share every Q and dO tile, copied once)
-// when the problem has enough key blocks to fill the GPU; otherwise each
-// part is a 4-wave workgroup of its own.  At d=256 the dK part alone (K, V,
-// the dK accumulator and the scores) needs ~350 registers, so the parts run
-// at one wave per SIMD.
+// At d=256 the dK part alone (K, V, the dK accumulator and the scores) needs
+// ~350 registers, so the parts run at one wave per SIMD.
+//
+// PART 3 and PART 4 are the two halves of one 8-wave workgroup (NW = 8: the
+// dV waves 0-3 and the dK waves 4-7 share every Q and dO tile, copied once),
+// used at d=128 when the problem has enough key blocks to fill the GPU.
+// There S is formed once: each tile runs in two phases split by a barrier.
+// In the first, a PART 3 wave forms S and the bf16 P of its 32 keys and
+// leaves P in LDS while its PART 4 partner (same keys) forms dP; in the
+// second, the PART 3 wave accumulates dV^T += dO^T P and the PART 4 wave
+// reads P, forms dS = P (dP - delta) and accumulates dK^T += Q^T dS.  Each
+// wave then runs two products per query block (the dK part three before),
+// and the pair's exponentials are taken once.
 //
 // GENERAL: Nq queries against Nk keys, causal mask offset by `off` (key j
 // visible to query i iff j <= i + off); otherwise Nk = Nq and off = 0.
@@ -276,7 +289,11 @@ __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __
   using G = Geo<D>;
   constexpr int kSteps = G::kSteps;
   constexpr int kDBlocks = G::kDBlocks;
-  constexpr bool kDoV = PART != 2, kDoK = PART != 1;
+  static_assert(PART >= 0 && PART <= 4, "PART");
+  static_assert(PART < 3 || NW == 2 * kWaves, "P is exchanged within an 8-wave workgroup");
+  constexpr bool kDoV = PART == 0 || PART == 1 || PART == 3;
+  constexpr bool kDoK = PART == 0 || PART == 2 || PART == 4;
+  constexpr bool kShare = PART >= 3;  // S formed once per pair, P exchanged through LDS
   constexpr int kQBlocks = kQT / kRows;       // 32-query blocks per tile
   constexpr int kTileBytes = kQT * G::kRowBytes;
   constexpr int kStageBytes = 2 * kTileBytes + 2 * kQT * 4;  // Q, dO, lse, delta
@@ -413,6 +430,88 @@ __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __
         }
       }
     };
+    // PART 3: S = Q K^T of the live query blocks, then P as bf16 B operands
+    // (0 where MASK hides an entry).  PART 4: dP = dO V^T of the live query
+    // blocks.  With both blocks live their two accumulator chains are
+    // interleaved, so neither MFMA waits on its predecessor's result.
+    auto prod2 = [&](const unsigned char* tile_lds, const bf16x8(&bop)[kSteps], bool live0, bool live1,
+                     f32x16(&acc)[kQBlocks]) __attribute__((always_inline)) {
+      static_assert(kQBlocks == 2, "two query blocks per tile");
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[qb][r] = 0.f;
+      if (live0 && live1) {
+        // All operand reads first: the products have no VALU work to hide
+        // LDS latency behind, so the reads run ahead of the MFMAs.
+        bf16x8 a0[kSteps], a1[kSteps];
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+          a0[st] = *reinterpret_cast<const bf16x8*>(tile_lds + ro[st]);
+          a1[st] = *reinterpret_cast<const bf16x8*>(tile_lds + kRows * G::kRowBytes + ro[st]);
+        }
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+          acc[0] = mfma(a0[st], bop[st], acc[0]);
+          acc[1] = mfma(a1[st], bop[st], acc[1]);
+        }
+        // Keep the reads ahead: six first, then two per pair of MFMAs (the
+        // scheduler otherwise places each read right before its product).
+        if constexpr (kSteps >= 4) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // DS reads
+#pragma unroll
+          for (int i = 0; i < kSteps - 3; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+        }
+      } else if (live0 || live1) {
+        const int qb = live0 ? 0 : 1;
+        const unsigned char* const a = tile_lds + qb * kRows * G::kRowBytes;
+        f32x16 one = acc[0];
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) one = mfma(*reinterpret_cast<const bf16x8*>(a + ro[st]), bop[st], one);
+        acc[qb] = one;
+      }
+    };
+    auto probs = [&](auto mask_tag, int qb, const f32x16& sacc, bf16x8(&pb)[2]) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qi = qb * kRows + 8 * g + 4 * half;  // tile row of registers 4g..4g+3
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_lds + qi);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * g + j;
+          float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], c, -l4[j]));
+          if constexpr (MASK) {
+            const int query = qt * kQT + qi + j;
+            const bool vis = CAUSAL ? (key0 + l32 <= query + off && query < Nq) : (query < Nq);
+            p = vis ? p : 0.f;
+          }
+          pb[r >> 3][r & 7] = (__bf16)p;
+        }
+      }
+    };
+    // PART 4: dS = P (dP - delta) from the exchanged bf16 P.
+    auto ds_from_p = [&](int qb, const bf16x8(&pb)[2], const f32x16& pacc, bf16x8(&sb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qi = qb * kRows + 8 * g + 4 * half;
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt_lds + qi);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * g + j;
+          sb[r >> 3][r & 7] = (__bf16)((float)pb[r >> 3][r & 7] * (pacc[r] - d4[j]));
+        }
+      }
+    };
+    // This lane's slot for chunk cc of query block qb of dV wave `wave`.
+    auto pslot = [&](int qb, int cc) __attribute__((always_inline)) {
+      return smem + 2 * kStageBytes + ((wave * kQBlocks + qb) * 2 + cc) * (kWave * 16) + lane * 16;
+    };
+
     // dV^T += dO^T P and dK^T += Q^T dS over the block's two 16-query steps.
     auto pv = [&](int qb, const bf16x8(&pb)[2], const bf16x8(&sb)[2]) __attribute__((always_inline)) {
       const unsigned char* const qa = qt_lds + qb * kRows * G::kRowBytes;
@@ -428,6 +527,52 @@ __device__ __forceinline__ void dkdv_body(const __bf16* __restrict__ q, const __
 
     const int qrow_first = qt * kQT;
     const bool interior = (!CAUSAL || qrow_first + off >= key0 + kRows - 1) && qrow_first + kQT <= Nq;
+    // Query block qb is skipped when no query of it sees a key of the wave
+    // (the same for both waves of a pair, which own the same keys).
+    auto skip = [&](int qb) __attribute__((always_inline)) {
+      const int qrow0 = qrow_first + qb * kRows;
+      return (CAUSAL && qrow0 + kRows - 1 + off < key0) || qrow0 >= Nq;
+    };
+    if constexpr (kShare) {
+      // Phase 1: S and P (PART 3, P left in LDS) / dP (PART 4).
+      const bool live0 = !skip(0), live1 = !skip(1);
+      bf16x8 pb[kQBlocks][2];
+      f32x16 acc2[kQBlocks];  // S (PART 3) or dP (PART 4)
+      if constexpr (PART == 3) {
+        set_prio<D>(1);
+        prod2(qt_lds, kf, live0, live1, acc2);
+#pragma unroll
+        for (int qb = 0; qb < kQBlocks; ++qb) {
+          if (!(qb ? live1 : live0)) continue;
+          if (interior) probs(std::false_type{}, qb, acc2[qb], pb[qb]);
+          else probs(std::true_type{}, qb, acc2[qb], pb[qb]);
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) *reinterpret_cast<bf16x8*>(pslot(qb, cc)) = pb[qb][cc];
+        }
+      } else {
+        prod2(dot_lds, vf, live0, live1, acc2);
+      }
+      if constexpr (PART == 3) set_prio<D>(0);
+      __syncthreads();  // every P of the tile is in LDS
+      // Phase 2: dV (PART 3) / dS and dK (PART 4).
+      if constexpr (PART == 4) set_prio<D>(1);
+#pragma unroll
+      for (int qb = 0; qb < kQBlocks; ++qb) {
+        if (!(qb ? live1 : live0)) continue;
+        if constexpr (PART == 3) {
+          pv(qb, pb[qb], pb[qb]);
+        } else {
+          bf16x8 pr[2], sb[2];
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) pr[cc] = *reinterpret_cast<const bf16x8*>(pslot(qb, cc));
+          ds_from_p(qb, pr, acc2[qb], sb);
+          pv(qb, sb, sb);
+        }
+      }
+      if constexpr (PART == 4) set_prio<D>(0);
+      if (qt + 1 < n_qt) publish_lse(s ^ 1);
+      return;
+    }
 #pragma unroll
     for (int qb = 0; qb < kQBlocks; ++qb) {
       const int qrow0 = qrow_first + qb * kRows;
@@ -518,13 +663,13 @@ void bwd_dkdv_pair_kernel(const __bf16* __restrict__ q, const __bf16* __restrict
                           const __bf16* __restrict__ dout, const float* __restrict__ delta,
                           __bf16* __restrict__ dk, __bf16* __restrict__ dv, int Nq, int Nk, int off,
                           float scale, float c) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[dkdv_smem_bytes<D>()];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[dkdv_pair_smem_bytes<D>()];
   const int lid = logical_block();
   if (__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) >= kWaves)
-    dkdv_body<D, CAUSAL, 2, GENERAL, 2 * kWaves>(q, k, v, lse, dout, delta, dk, dv, Nq, Nk, off, scale,
+    dkdv_body<D, CAUSAL, 4, GENERAL, 2 * kWaves>(q, k, v, lse, dout, delta, dk, dv, Nq, Nk, off, scale,
                                                  c, smem, lid);
   else
-    dkdv_body<D, CAUSAL, 1, GENERAL, 2 * kWaves>(q, k, v, lse, dout, delta, dk, dv, Nq, Nk, off, scale,
+    dkdv_body<D, CAUSAL, 3, GENERAL, 2 * kWaves>(q, k, v, lse, dout, delta, dk, dv, Nq, Nk, off, scale,
                                                  c, smem, lid);
 }
 
