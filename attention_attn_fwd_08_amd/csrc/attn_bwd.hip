@@ -652,10 +652,12 @@ void bwd_dkdv_split_kernel(const __bf16* __restrict__ q, const __bf16* __restric
 
 // d=128 with at least one key block per CU: one 8-wave workgroup per key
 // block, waves 0-3 computing dV and waves 4-7 dK over the same Q and dO tiles
-// in LDS (copied once for both parts; 66.5 KB of LDS per CU instead of two
-// workgroups' 133 KB).  Measured 4 % faster than the two-workgroup form on
-// B16-H16-N4096 and B4-H32-N8192 causal, slower on problems with fewer key
-// blocks than CUs (half as many workgroups to spread).
+// in LDS (copied once for both parts; 81 KB of LDS per CU with the P
+// exchange, instead of two workgroups' 133 KB), S formed once per pair.
+// Sharing the tiles measured 4 % faster than the two-workgroup form on
+// B16-H16-N4096 and B4-H32-N8192 causal, and forming S once a further 0-6 %
+// (most with causal masks); with fewer key blocks than CUs the two-workgroup
+// form wins (twice as many workgroups to spread).
 template <int D, bool CAUSAL, bool GENERAL>
 __global__ __launch_bounds__(2 * kWaves * kWave, 1)
 void bwd_dkdv_pair_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
