@@ -36,9 +36,11 @@ def _poison_lib():
 
 
 # (B, H, Nq, Nk, d, causal, splits): square shapes (persistent at d=128/256
-# with more tiles than CUs, ragged tails), general shapes and split-KV.
+# with more tiles than CUs, and at d=64 causal with 2 to 4 rounds of
+# workgroups; ragged tails), general shapes and split-KV.
 CASES = [
     (1, 40, 1800, 1800, 128, True, 0),
+    (2, 40, 3000, 3000, 64, True, 0),
     (2, 3, 700, 700, 128, False, 0),
     (1, 20, 1700, 1700, 256, True, 0),
     (2, 3, 333, 333, 64, True, 0),

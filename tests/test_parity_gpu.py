@@ -95,7 +95,9 @@ def test_workload_sampled(name):
 # more query tiles than the GPU has compute units run one persistent
 # workgroup per CU, each walking several query tiles (the schedule's slots per
 # XCD do not divide these tile counts, and the last query tile of every head
-# is partial).
+# is partial).  Square causal problems at d=64 run persistent with 2 to 4
+# rounds of workgroups: the three d=64 cases have 1920-2048 query tiles of
+# 128, inside that window with two or three workgroups per CU.
 PERSISTENT = [
     # B, H, N, d, causal
     (1, 40, 1800, 128, False),
@@ -105,6 +107,9 @@ PERSISTENT = [
     (1, 300, 256, 128, True),
     (1, 20, 1700, 256, False),
     (1, 20, 1700, 256, True),
+    (2, 40, 3000, 64, True),
+    (1, 100, 2500, 64, True),
+    (16, 16, 1024, 64, True),
 ]
 
 
