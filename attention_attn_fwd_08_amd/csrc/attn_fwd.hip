@@ -665,15 +665,20 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
   // head dims that run one workgroup per CU: one persistent workgroup per CU,
   // so a CU is not idle while one workgroup drains and the next starts.
   // Where several workgroups share a CU (d = 32, 64, 96) they already cover
-  // each other's start-up, and the persistent form measured slower -- except
-  // square causal problems at d=64 with 2 to 4 rounds of workgroups, whose
-  // tiles of unequal length leave a ragged last round that the persistent
-  // schedule (long and short tiles paired per slot) evens out: measured +1 to
-  // +12 % there, -1.5 % at 1.3 and 5.3 rounds, and no gain without a mask.
-  if constexpr (D == 128 || D == 256 || (D == 64 && CAUSAL && !GENERAL)) {
+  // each other's start-up, and the persistent form measured no better on
+  // problems without a mask.  Square causal problems with few rounds of
+  // workgroups (query tiles over resident slots) are the exception: their
+  // tiles of unequal length leave a ragged last round, which the persistent
+  // schedule (long and short tiles paired per slot) evens out.  Measured
+  // (same box, always persistent against never): d=32 +9 to +29 % at 1.5-3
+  // rounds, +1 % at 4, -2 % at 8; d=64 +1 to +12 % at 2.7-4 rounds, -1.5 % at
+  // 1.3 and 5.3; d=96 +4 to +29 % at 1.5-8 rounds, +0.2 % at 16.
+  if constexpr (D == 128 || D == 256 || (CAUSAL && !GENERAL)) {
     const int grid = persistent_grid<D, CAUSAL, GENERAL>(dev, n_cu);
     bool persist = grid > 0 && n_work > grid;
-    if constexpr (D == 64) persist = grid > 0 && n_work > 2 * grid && n_work <= 4 * grid;
+    if constexpr (D == 32) persist = persist && n_work <= 4 * grid;
+    if constexpr (D == 64) persist = persist && n_work > 2 * grid && n_work <= 4 * grid;
+    if constexpr (D == 96) persist = persist && n_work <= 8 * grid;
     if (persist) {
       hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, GENERAL, false, true>), dim3(grid),
                          dim3(Launch<D>::kThreads), 0, stream, static_cast<const __bf16*>(q),

@@ -36,11 +36,13 @@ def _poison_lib():
 
 
 # (B, H, Nq, Nk, d, causal, splits): square shapes (persistent at d=128/256
-# with more tiles than CUs, and at d=64 causal with 2 to 4 rounds of
+# with more tiles than CUs, and at d=32, 64 and 96 causal with few rounds of
 # workgroups; ragged tails), general shapes and split-KV.
 CASES = [
     (1, 40, 1800, 1800, 128, True, 0),
     (2, 40, 3000, 3000, 64, True, 0),
+    (3, 32, 2000, 2000, 32, True, 0),
+    (2, 40, 1500, 1500, 96, True, 0),
     (2, 3, 700, 700, 128, False, 0),
     (1, 20, 1700, 1700, 256, True, 0),
     (2, 3, 333, 333, 64, True, 0),

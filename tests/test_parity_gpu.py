@@ -95,9 +95,11 @@ def test_workload_sampled(name):
 # more query tiles than the GPU has compute units run one persistent
 # workgroup per CU, each walking several query tiles (the schedule's slots per
 # XCD do not divide these tile counts, and the last query tile of every head
-# is partial).  Square causal problems at d=64 run persistent with 2 to 4
-# rounds of workgroups: the three d=64 cases have 1920-2048 query tiles of
-# 128, inside that window with two or three workgroups per CU.
+# is partial).  Square causal problems at d=32, 64 and 96 run persistent with
+# few rounds of workgroups (query tiles over resident slots; at most 4 at
+# d=32, 2 to 4 at d=64, at most 8 at d=96): the d=64 cases have 1920-2048
+# query tiles of 128, the d=32 case 1536 and the d=96 case 960, inside those
+# windows at any plausible number of workgroups per CU.
 PERSISTENT = [
     # B, H, N, d, causal
     (1, 40, 1800, 128, False),
@@ -110,6 +112,8 @@ PERSISTENT = [
     (2, 40, 3000, 64, True),
     (1, 100, 2500, 64, True),
     (16, 16, 1024, 64, True),
+    (3, 32, 2000, 32, True),
+    (2, 40, 1500, 96, True),
 ]
 
 
