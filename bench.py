@@ -419,7 +419,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build is a single-GPU kernel "
+        print("bench.py measures one GPU only: the kernels run on a single GPU "
               "(--gpus 1); multi-GPU runs are not supported.", file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0:
