@@ -52,6 +52,8 @@
 //     it walks its XCD's tiles and issues the next tile's K/V/Q loads before
 //     storing the current tile's output, so the CU does not idle between
 //     tiles; causal rounds alternate long and short tiles per workgroup.
+//     Square causal problems at d=32, 64 and 96 with few rounds of
+//     workgroups run persistent too, which evens out a ragged last round.
 
 #include <hip/hip_runtime.h>
 
