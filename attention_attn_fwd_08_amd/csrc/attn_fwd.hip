@@ -52,8 +52,9 @@
 //     it walks its XCD's tiles and issues the next tile's K/V/Q loads before
 //     storing the current tile's output, so the CU does not idle between
 //     tiles; causal rounds alternate long and short tiles per workgroup.
-//     Square causal problems at d=32, 64 and 96 with few rounds of
-//     workgroups run persistent too, which evens out a ragged last round.
+//     Causal problems at d=32, 64 and 96 with few rounds of workgroups
+//     (square, or Nq <= Nk) run persistent too, which evens out a ragged
+//     last round.
 
 #include <hip/hip_runtime.h>
 
@@ -668,16 +669,19 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
   // so a CU is not idle while one workgroup drains and the next starts.
   // Where several workgroups share a CU (d = 32, 64, 96) they already cover
   // each other's start-up, and the persistent form measured no better on
-  // problems without a mask.  Square causal problems with few rounds of
-  // workgroups (query tiles over resident slots) are the exception: their
-  // tiles of unequal length leave a ragged last round, which the persistent
-  // schedule (long and short tiles paired per slot) evens out.  Measured
-  // (same box, always persistent against never): d=32 +9 to +29 % at 1.5-3
+  // problems without a mask.  Causal problems with few rounds of workgroups
+  // (query tiles over resident slots) are the exception: their tiles of
+  // unequal length leave a ragged last round, which the persistent schedule
+  // (long and short tiles paired per slot) evens out.  Measured (same box,
+  // always persistent against never), square: d=32 +9 to +29 % at 1.5-3
   // rounds, +1 % at 4, -2 % at 8; d=64 +1 to +12 % at 2.7-4 rounds, -1.5 % at
-  // 1.3 and 5.3; d=96 +4 to +29 % at 1.5-8 rounds, +0.2 % at 16.
-  if constexpr (D == 128 || D == 256 || (CAUSAL && !GENERAL)) {
+  // 1.3 and 5.3; d=96 +4 to +29 % at 1.5-8 rounds, +0.2 % at 16.  General
+  // shapes with Nq <= Nk (queries at the end of a longer key range): +3 to
+  // +11 % at 2-2.7 rounds, +1 % at 4; with Nq > Nk -6 %, so not there.
+  if constexpr (D == 128 || D == 256 || CAUSAL) {
     const int grid = persistent_grid<D, CAUSAL, GENERAL>(dev, n_cu);
     bool persist = grid > 0 && n_work > grid;
+    if constexpr (GENERAL && D != 128 && D != 256) persist = persist && Nq <= Nk;
     if constexpr (D == 32) persist = persist && n_work <= 4 * grid;
     if constexpr (D == 64) persist = persist && n_work > 2 * grid && n_work <= 4 * grid;
     if constexpr (D == 96) persist = persist && n_work <= 8 * grid;

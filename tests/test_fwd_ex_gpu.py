@@ -76,7 +76,11 @@ def test_fwd_ex_square_is_attn_fwd(causal):
 # At d=128 and d=256, problems with more query tiles than the GPU has compute
 # units run one persistent workgroup per CU.  These general shapes include
 # query tiles that see no key at all (Nq > Nk, causal) and partial last tiles
-# whose waves past Nq compute nothing; both continue to the next tile.
+# whose waves past Nq compute nothing; both continue to the next tile.  At
+# d=32, 64 and 96 causal problems with Nq <= Nk and few rounds of workgroups
+# run persistent too: the last three cases have 1536, 2048 and 960 query
+# tiles of 128, inside those windows at any plausible number of workgroups
+# per CU.
 PERSISTENT = [
     # (B, H, Nq, Nk, d, causal)
     (1, 40, 1800, 2600, 128, True),
@@ -84,6 +88,9 @@ PERSISTENT = [
     (1, 50, 700, 3000, 128, False),
     (1, 20, 1700, 2100, 256, True),
     (1, 24, 2100, 1500, 256, True),
+    (1, 192, 1024, 2048, 32, True),
+    (1, 128, 2000, 2600, 64, True),
+    (1, 80, 1500, 2000, 96, True),
 ]
 
 

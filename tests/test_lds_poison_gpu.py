@@ -43,6 +43,7 @@ CASES = [
     (2, 40, 3000, 3000, 64, True, 0),
     (3, 32, 2000, 2000, 32, True, 0),
     (2, 40, 1500, 1500, 96, True, 0),
+    (1, 80, 1500, 2000, 96, True, 0),
     (2, 3, 700, 700, 128, False, 0),
     (1, 20, 1700, 1700, 256, True, 0),
     (2, 3, 333, 333, 64, True, 0),

@@ -197,6 +197,7 @@ FORCED = [
     (1, 128, 1600, 1600, 64, True, 0, 2.0),  # persistent at d=64 (1664 causal query tiles)
     (3, 32, 2000, 2000, 32, True, 0, 1.0),   # persistent at d=32 (1536)
     (2, 40, 1500, 1500, 96, True, 0, 1.0),   # persistent at d=96 (960)
+    (1, 80, 1500, 2000, 96, True, 0, 1.0),   # persistent, general shape (960)
     (1, 2, 257, 257, 32, False, 0, 1.0),
     (1, 2, 300, 300, 96, True, 0, 1.0),
     (1, 3, 100, 900, 128, True, 0, 1.0),
