@@ -78,3 +78,46 @@ def test_random_backward(B, H, Nq, Nk, d, causal, seed):
     what = f"B{B}H{H}Nq{Nq}Nk{Nk}d{d}c{int(causal)}"
     check_grads(got, ref, what)
     check_delta(got[3], o, g, what)
+
+
+def _window_cases(n, seed):
+    """Causal shapes at d=32/64/96 with hundreds to thousands of 128-query
+    tiles, so that the persistent windows (few rounds of workgroups) and
+    their edges are crossed: square, or a query block at the end of a longer
+    key range."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        d = int(rng.choice([32, 64, 96]))
+        H = int(rng.integers(40, 201))
+        Nq = int(rng.integers(600, 3001))
+        Nk = Nq if rng.integers(0, 2) else Nq + int(rng.integers(1, 2001))
+        out.append((1, H, Nq, Nk, d, int(rng.integers(0, 1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,seed", _window_cases(12, 76))
+def test_random_persistent_windows(B, H, Nq, Nk, d, seed):
+    import torch
+    import attention_attn_fwd_08_amd as af
+    log(f"random window B{B} H{H} Nq{Nq} Nk{Nk} d{d} ({B * H * ((Nq + 127) // 128)} query tiles)")
+    qb, kb, vb = _inputs(B, H, Nq, Nk, d, seed)
+    scale = 1.0 / np.sqrt(d)
+    q, k, v = to_device(qb), to_device(kb), to_device(vb)
+    o, lse = af.attn_fwd_ex(q, k, v, causal=True, scale=scale)
+    # Every row written, and the same bits again into NaN-filled outputs.
+    o2 = torch.full_like(o, float("nan"))
+    lse2 = torch.full_like(lse, float("nan"))
+    af.attn_fwd_ex(q, k, v, causal=True, scale=scale, out=o2, lse=lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(lse2, lse)
+    # Rows at query-tile edges and random rows of every head.
+    rng = np.random.default_rng(seed ^ 0x5A5A)
+    rows = []
+    for bh in range(B * H):
+        picks = {0, 127, 128, Nq - 1} | set(int(x) for x in rng.integers(0, Nq, 3))
+        rows += [bh * Nq + i for i in sorted(picks) if 0 <= i < Nq]
+    rows = np.asarray(rows, dtype=np.int64)
+    o_ref, lse_ref = oracle.attention_ex_rows(qb, kb, vb, True, scale, rows, threads=ORACLE_THREADS)
+    idx = torch.from_numpy(rows).to(o.device)
+    _check_fwd(o.reshape(-1, d)[idx], lse.reshape(-1)[idx], o_ref, lse_ref)
