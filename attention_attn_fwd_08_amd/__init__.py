@@ -31,7 +31,7 @@ __all__ = ["attn_fwd", "attn_fwd_raw", "attn_fwd_ex", "attn_fwd_ex_raw", "attn_f
            "attn_fwd_splitkv_raw", "attn_fwd_splitkv_noalloc", "attn_fwd_splitkv_noalloc_raw",
            "splitkv_splits", "attn_bwd",
            "attn_bwd_raw", "attn_bwd_ex", "attn_bwd_ex_raw", "gemm", "gemm_raw", "GEMM_NN", "GEMM_NT", "attn_fwd_strerror",
-           "load_library", "LIBRARY", "Status", "AttnError"]
+           "load_library", "LIBRARY", "Status", "AttnError", "attention"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_HERE, "libattn_fwd.so")
@@ -482,3 +482,42 @@ def gemm(a, b, layout: str = "nn", out=None):
     if status != Status.OK:
         raise AttnError(status, attn_fwd_strerror(status))
     return out
+
+
+def _attention_function():
+    """The autograd Function behind :func:`attention`, built on first use so
+    that importing the package does not import torch."""
+    import torch
+
+    class _Attention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, causal, scale):
+            o, lse = attn_fwd_ex(q, k, v, causal=causal, scale=scale)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.causal, ctx.scale = causal, scale
+            return o
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, o, lse = ctx.saved_tensors
+            dq, dk, dv, _ = attn_bwd_ex(q, k, v, o, lse, dout.contiguous(), causal=ctx.causal,
+                                        scale=ctx.scale)
+            return dq, dk, dv, None, None
+
+    return _Attention
+
+
+_ATTENTION = None
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None):
+    """``softmax(scale * q k^T) v`` with autograd: q [B, H, Nq, d] and k, v
+    [B, H, Nk, d] bf16 on the GPU (bottom-right causal mask when Nq != Nk).
+    The forward runs :func:`attn_fwd_ex` and keeps its O and log-sum-exp; the
+    backward runs :func:`attn_bwd_ex` on them.  Returns o, bf16 [B, H, Nq, d]."""
+    global _ATTENTION
+    if _ATTENTION is None:
+        _ATTENTION = _attention_function()
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    return _ATTENTION.apply(q, k, v, bool(causal), float(scale))

@@ -136,6 +136,9 @@ def test_python_binding_rejects_cpu_tensors():
         af.attn_fwd(x, x, x)
     with pytest.raises(TypeError):
         af.attn_fwd(x.float(), x, x)
+    # The autograd entry checks through the same forward binding.
+    with pytest.raises(ValueError):
+        af.attention(x, x, x)
 
 
 def test_no_undefined_kernel_stubs(lib):
